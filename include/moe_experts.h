@@ -1,0 +1,179 @@
+/*
+ * moe_experts.h -- C ABI of the MI355X (gfx950) routed top-k experts forward.
+ *
+ * What is computed (Hugging Face Transformers docs, "Experts backends" page,
+ * introduction): for each token a router has chosen k experts; the token's hidden
+ * state is projected through each chosen expert and the k results are summed with
+ * the routing weights.  The expert is a gated MLP -- gate/up projection, SwiGLU,
+ * down projection (same page, backend table "deepgemm_megamoe" row and the
+ * "SonicMoE" section, where silu maps to SwiGLU):
+ *
+ *     out[t,:] = sum_{j<k} w[t,j] * W_down[e] ( silu(W_gate[e] x_t) * (W_up[e] x_t) ),
+ *     e = idx[t,j],  silu(z) = z / (1 + exp(-z)).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers, row-major, contiguous, 16-byte
+ *     aligned, owned by the caller.  The library never frees or retains them.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     on it and the call returns without waiting, except where stated.
+ *   - Every argument is validated on the host before the first HIP call; on a
+ *     validation error nothing is enqueued and no output is written.
+ *   - The library allocates no device memory per call: scratch comes from the
+ *     caller's workspace (size from moe_workspace_size).  Its only state is a
+ *     lazily built per-device record (CU count), made on the first call on a
+ *     device (the page's "DeepGEMM" section loads its kernel lazily as well).
+ *   - Calls on one stream are ordered; two calls that share a workspace must not
+ *     overlap in time.
+ */
+#ifndef MOE_EXPERTS_H
+#define MOE_EXPERTS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL_ARG = 1,            /* a required pointer is NULL                     */
+  MOE_ERR_BAD_SHAPE = 2,           /* sizes out of range / not multiples / misaligned */
+  MOE_ERR_UNSUPPORTED = 3,         /* dtype / scale-format combination not provided  */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 4, /* workspace_bytes < moe_workspace_size()         */
+  MOE_ERR_BAD_INDEX = 5,           /* an expert id outside [0, E) (CHECK_INDICES)    */
+  MOE_ERR_HIP = 6                  /* a HIP runtime call failed                      */
+} moe_status;
+
+typedef enum {
+  MOE_F32 = 0,      /* IEEE binary32                                   */
+  MOE_BF16 = 1,     /* bfloat16                                        */
+  MOE_FP8_E4M3 = 2  /* OCP 8-bit E4M3 ("e4m3fn": max 448, no infinity) */
+} moe_dtype;
+
+typedef enum {
+  MOE_SCALE_NONE = 0,
+  MOE_SCALE_F32 = 1,   /* one float32 scale per 128x128 weight block               */
+  MOE_SCALE_UE8M0 = 2  /* one uint8 exponent b per block, scale = 2^(b-127)        */
+} moe_scale_fmt;
+
+enum {
+  /* Synchronise `stream` after the forward and return MOE_ERR_BAD_INDEX if any
+   * topk_idx entry was outside [0, E).  Without it such a slot contributes
+   * nothing and the call still returns MOE_OK. */
+  MOE_FLAG_CHECK_INDICES = 1u,
+  /* Bit-reproducible combine: each slot's weighted expert output is written to
+   * its own row and the k rows of a token are summed in slot order, instead of
+   * floating-point atomic adds (needs the larger workspace). */
+  MOE_FLAG_DETERMINISTIC = 2u,
+  /* Path selection (both give the same result within tolerance): the grouped
+   * path sorts slots by expert and runs grouped GEMMs; the decode path streams
+   * each selected expert's weights once against its few tokens.  Default: decode
+   * when T <= 64, grouped otherwise. */
+  MOE_FLAG_FORCE_GROUPED = 4u,
+  MOE_FLAG_FORCE_DECODE = 8u
+};
+
+/* Problem description (plain values; no pointers). */
+typedef struct {
+  int64_t T;            /* tokens, >= 0                                              */
+  int32_t H;            /* hidden size                                               */
+  int32_t I;            /* expert intermediate size                                  */
+  int32_t E;            /* number of experts, 1..1024                                */
+  int32_t k;            /* experts per token, 1..E                                   */
+  int32_t act_dtype;    /* moe_dtype of hidden and out: MOE_F32 or MOE_BF16          */
+  int32_t weight_dtype; /* moe_dtype of the weights: MOE_F32 (with act MOE_F32),
+                           MOE_BF16 (with act MOE_BF16), MOE_FP8_E4M3 (act MOE_BF16) */
+  int32_t scale_fmt;    /* moe_scale_fmt: != NONE exactly when weights are fp8       */
+  uint32_t flags;       /* MOE_FLAG_*                                                */
+} moe_problem;
+
+/* Shape rules checked by every call taking a moe_problem:
+ *   H % 128 == 0, I % 64 == 0 (f32, bf16 weights); H % 128 == 0, I % 128 == 0 (fp8);
+ *   1 <= E <= 1024, 1 <= k <= E, T * k < 2^31, H, I <= 65536.                      */
+
+/* ABI version of the loaded library (MOE_ABI_VERSION). */
+int moe_abi_version(void);
+
+/* Human-readable name of a status code (static string). */
+const char* moe_status_str(moe_status s);
+
+/* Bytes of device workspace moe_experts_forward needs for problem *p (host only,
+ * closed form, no HIP call).  Grows with T*k*(I + H) and T*H; with
+ * MOE_FLAG_DETERMINISTIC it also holds a float32 [T*k, H] buffer. */
+moe_status moe_workspace_size(const moe_problem* p, size_t* bytes);
+
+/*
+ * The routed top-k experts forward.
+ *
+ *   hidden          [T, H]        act_dtype
+ *   topk_idx        [T, k] int32  chosen expert ids, 0 <= id < E (a repeated id in
+ *                                 one row counts once per slot)
+ *   topk_w          [T, k] float32 routing weights (used as given; no renormalising)
+ *   w_gate_up       [E, 2I, H]    weight_dtype; rows [0, I) of expert e are the gate
+ *                                 projection, rows [I, 2I) the up projection
+ *   w_down          [E, H, I]     weight_dtype
+ *   w_gate_up_scale [E, 2I/128, H/128]  fp8 only: float32, or uint8 for UE8M0; NULL otherwise
+ *   w_down_scale    [E, H/128, I/128]   fp8 only; NULL otherwise
+ *   out             [T, H]        act_dtype; overwritten (never accumulated into)
+ *   workspace       device scratch of workspace_bytes >= moe_workspace_size(p)
+ *
+ * fp8 weights (page section "FP8 and FP4 quantized experts" and its note: float32
+ * or UE8M0 block scales consumed directly; dynamic per-row activation scales):
+ * the bf16 hidden states are quantised per token and per 128 channels to e4m3
+ * with a float32 scale amax/448, and so is the SwiGLU output before the down
+ * projection; weight block (r, c) dequantises to code * scale[r/128][c/128].
+ *
+ * Returns MOE_OK once the work is enqueued (T == 0: nothing is enqueued).
+ * Errors: NULL_ARG, BAD_SHAPE, UNSUPPORTED, WORKSPACE_TOO_SMALL before any HIP
+ * call; BAD_INDEX only with MOE_FLAG_CHECK_INDICES (after a stream sync); HIP.
+ */
+moe_status moe_experts_forward(const moe_problem* p, const void* hidden, const int32_t* topk_idx,
+                               const float* topk_w, const void* w_gate_up, const void* w_down,
+                               const void* w_gate_up_scale, const void* w_down_scale, void* out,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Routing bookkeeping alone: the stable sort of the T*k slots a = t*k + j by
+ * chosen expert (page backend table, "grouped_mm" row: tokens are sorted by
+ * their selected expert before one grouped GEMM).
+ *
+ *   counts  [E]   int32  slots choosing expert e
+ *   offsets [E+1] int32  exclusive prefix sum of counts (offsets[E] = valid slots)
+ *   perm    [T*k] int32  perm[p] = the slot at sorted position p; slots of one
+ *                        expert stay in increasing slot order
+ *   inv     [T*k] int32  inv[perm[p]] = p; -1 for a slot whose id is out of range
+ *
+ * Same workspace rules as moe_experts_forward (size from moe_workspace_size).
+ * Out-of-range ids are left out of every output; with MOE_FLAG_CHECK_INDICES
+ * the call synchronises and returns MOE_ERR_BAD_INDEX if there were any.
+ */
+moe_status moe_route(const moe_problem* p, const int32_t* topk_idx, int32_t* counts,
+                     int32_t* offsets, int32_t* perm, int32_t* inv, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/*
+ * Dynamic per-row e4m3 quantisation (page section "FP8 and FP4 quantized
+ * experts": per-row activation scales, static per-tensor scales rejected).
+ * For each row and each group of 128 consecutive columns:
+ *   amax = max |x| (float32), s = amax / 448 (float32, correctly rounded; 1 if
+ *   amax == 0), q = e4m3(x / s) (float32 division, round to nearest even,
+ *   saturating at +-448).
+ *
+ *   x_bf16 [rows, cols] bf16;  q [rows, cols] uint8 e4m3 codes;
+ *   scales [rows, cols/128] float32.   cols % 128 == 0, rows >= 0.
+ */
+moe_status moe_quantize_rows_fp8(const void* x_bf16, int64_t rows, int32_t cols, uint8_t* q,
+                                 float* scales, void* stream);
+
+/* Describe the plan (path, tile shapes, workspace) chosen for *p into buf (NUL
+ * terminated, truncated to len).  Host only. */
+moe_status moe_plan_describe(const moe_problem* p, char* buf, size_t len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_EXPERTS_H */

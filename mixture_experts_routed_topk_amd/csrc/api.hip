@@ -1,0 +1,356 @@
+// C ABI of the routed top-k experts forward: argument validation (before any HIP
+// call, so every error path is testable without a GPU), the workspace carve-up,
+// the lazy per-device record, path selection and the kernel launches.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/moe_experts.h"
+#include "internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr int64_t kDecodeMaxTokens = 64;
+
+struct DeviceRecord {
+  bool ready = false;
+  int cus = 0;
+};
+DeviceRecord g_devices[kMaxDevices];
+std::mutex g_devices_mu;
+
+// ---------------------------------------------------------------------------- validation
+
+bool is_fp8(const moe_problem& p) { return p.weight_dtype == MOE_FP8_E4M3; }
+
+moe_status validate_problem(const moe_problem* p) {
+  if (!p) return MOE_ERR_NULL_ARG;
+  const bool combo_f32 = p->act_dtype == MOE_F32 && p->weight_dtype == MOE_F32 && p->scale_fmt == MOE_SCALE_NONE;
+  const bool combo_bf16 = p->act_dtype == MOE_BF16 && p->weight_dtype == MOE_BF16 && p->scale_fmt == MOE_SCALE_NONE;
+  const bool combo_fp8 = p->act_dtype == MOE_BF16 && p->weight_dtype == MOE_FP8_E4M3 &&
+                         (p->scale_fmt == MOE_SCALE_F32 || p->scale_fmt == MOE_SCALE_UE8M0);
+  if (!(combo_f32 || combo_bf16 || combo_fp8)) return MOE_ERR_UNSUPPORTED;
+  const uint32_t known = MOE_FLAG_CHECK_INDICES | MOE_FLAG_DETERMINISTIC | MOE_FLAG_FORCE_GROUPED |
+                         MOE_FLAG_FORCE_DECODE;
+  if (p->flags & ~known) return MOE_ERR_UNSUPPORTED;
+  if ((p->flags & MOE_FLAG_FORCE_GROUPED) && (p->flags & MOE_FLAG_FORCE_DECODE)) return MOE_ERR_UNSUPPORTED;
+  if (p->T < 0 || p->E < 1 || p->E > 1024 || p->k < 1 || p->k > p->E) return MOE_ERR_BAD_SHAPE;
+  if (p->H <= 0 || p->I <= 0 || p->H > 65536 || p->I > 65536) return MOE_ERR_BAD_SHAPE;
+  if (p->H % 128 != 0) return MOE_ERR_BAD_SHAPE;
+  if (p->I % (is_fp8(*p) ? 128 : 64) != 0) return MOE_ERR_BAD_SHAPE;
+  const int64_t A = p->T * (int64_t)p->k;
+  if (A >= (int64_t(1) << 31)) return MOE_ERR_BAD_SHAPE;
+  // work-item counts of the grouped kernels must fit in int32
+  const int64_t items_gu = max_mtiles(A, p->E, 64) * (2 * (int64_t)p->I / 64);
+  const int64_t items_dn = max_mtiles(A, p->E, 64) * ((int64_t)p->H / 64);
+  if (items_gu >= (int64_t(1) << 31) || items_dn >= (int64_t(1) << 31)) return MOE_ERR_BAD_SHAPE;
+  return MOE_OK;
+}
+
+bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; }
+bool aligned4(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 3u) == 0; }
+
+// ---------------------------------------------------------------------------- plan
+
+enum Path { kGrouped = 0, kDecode = 1 };
+
+struct Plan {
+  Path path;
+  int bm_gu, bm_dn;  // grouped tile heights
+};
+
+Plan make_plan(const moe_problem& p) {
+  Plan pl;
+  bool decode = p.T <= kDecodeMaxTokens;
+  if (p.flags & MOE_FLAG_FORCE_GROUPED) decode = false;
+  if (p.flags & MOE_FLAG_FORCE_DECODE) decode = true;
+  pl.path = decode ? kDecode : kGrouped;
+  if (p.weight_dtype == MOE_F32) {
+    pl.bm_gu = gateup_f32_bm();
+    pl.bm_dn = down_f32_bm();
+  } else {
+    pl.bm_gu = gateup_bf16_bm();
+    pl.bm_dn = down_bf16_bm();
+  }
+  return pl;
+}
+
+// ---------------------------------------------------------------------------- workspace
+
+struct Layout {
+  size_t bad, counts, offsets, mt0, mt1, perm, inv, act, acc, slots, total;
+};
+
+size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
+
+Layout make_layout(const moe_problem& p) {
+  const size_t A = (size_t)p.T * p.k, E = p.E;
+  Layout L;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = up256(o + bytes);
+    return at;
+  };
+  L.bad = take(4);
+  L.counts = take(4 * E);
+  L.offsets = take(4 * (E + 1));
+  L.mt0 = take(4 * (E + 1));
+  L.mt1 = take(4 * (E + 1));
+  L.perm = take(4 * A);
+  L.inv = take(4 * A);
+  const size_t act_elem = p.weight_dtype == MOE_F32 ? 4 : 2;
+  L.act = take(act_elem * A * p.I);
+  const bool det = p.flags & MOE_FLAG_DETERMINISTIC;
+  L.acc = det ? o : take(4 * (size_t)p.T * p.H);
+  L.slots = det ? take(4 * A * p.H) : o;
+  L.total = o;
+  return L;
+}
+
+// ---------------------------------------------------------------------------- device
+
+moe_status device_record(DeviceRecord** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_devices_mu);
+  DeviceRecord& r = g_devices[dev];
+  if (!r.ready) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return MOE_ERR_HIP;
+    r.cus = cus > 0 ? cus : 1;
+    r.ready = true;
+  }
+  *out = &r;
+  return MOE_OK;
+}
+
+int id_bits(int E) {
+  int b = 0;
+  while ((1 << b) < E) ++b;
+  return b;
+}
+
+int persistent_grid(int cus, int per_cu, int64_t max_items) {
+  int64_t g = (int64_t)cus * per_cu;
+  if (max_items < g) g = max_items;
+  g = (g + 7) / 8 * 8;
+  return (int)(g < 8 ? 8 : g);
+}
+
+#define MOE_HIP_CHECK(expr)                  \
+  do {                                       \
+    if ((expr) != hipSuccess) return MOE_ERR_HIP; \
+  } while (0)
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL_ARG: return "null argument";
+    case MOE_ERR_BAD_SHAPE: return "bad shape, size or alignment";
+    case MOE_ERR_UNSUPPORTED: return "unsupported dtype, scale format or flag combination";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MOE_ERR_BAD_INDEX: return "expert id outside [0, E)";
+    case MOE_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+moe_status moe_workspace_size(const moe_problem* p, size_t* bytes) {
+  const moe_status st = validate_problem(p);
+  if (st != MOE_OK) return st;
+  if (!bytes) return MOE_ERR_NULL_ARG;
+  *bytes = make_layout(*p).total;
+  return MOE_OK;
+}
+
+moe_status moe_plan_describe(const moe_problem* p, char* buf, size_t len) {
+  const moe_status st = validate_problem(p);
+  if (st != MOE_OK) return st;
+  if (!buf || len == 0) return MOE_ERR_NULL_ARG;
+  const Plan pl = make_plan(*p);
+  const Layout L = make_layout(*p);
+  const char* wname = p->weight_dtype == MOE_F32 ? "f32" : (p->weight_dtype == MOE_BF16 ? "bf16" : "fp8_e4m3");
+  const char* sname = p->scale_fmt == MOE_SCALE_F32 ? "f32" : (p->scale_fmt == MOE_SCALE_UE8M0 ? "ue8m0" : "none");
+  snprintf(buf, len,
+           "path=%s weights=%s scales=%s gate_up_tile=%dx%d down_tile=%dx%d combine=%s workspace_bytes=%zu",
+           pl.path == kDecode ? "decode" : "grouped", wname, sname, pl.bm_gu,
+           p->weight_dtype == MOE_F32 ? 64 : 128, pl.bm_dn, p->weight_dtype == MOE_F32 ? 64 : 128,
+           (p->flags & MOE_FLAG_DETERMINISTIC) ? "slot_rows" : "atomic_f32", L.total);
+  return MOE_OK;
+}
+
+moe_status moe_route(const moe_problem* p, const int32_t* topk_idx, int32_t* counts, int32_t* offsets, int32_t* perm,
+                     int32_t* inv, void* workspace, size_t workspace_bytes, void* stream) {
+  moe_status st = validate_problem(p);
+  if (st != MOE_OK) return st;
+  if (!counts || !offsets || !workspace) return MOE_ERR_NULL_ARG;
+  if (p->T > 0 && (!topk_idx || !perm || !inv)) return MOE_ERR_NULL_ARG;
+  if (!aligned4(topk_idx) || !aligned4(counts) || !aligned4(offsets) || !aligned4(perm) || !aligned4(inv) ||
+      !aligned16(workspace))
+    return MOE_ERR_BAD_SHAPE;
+  const Layout L = make_layout(*p);
+  if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  DeviceRecord* dev = nullptr;
+  if ((st = device_record(&dev)) != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  RouteArgs r{};
+  r.idx = topk_idx;
+  r.A = (int)(p->T * p->k);
+  r.E = p->E;
+  r.id_bits = id_bits(p->E);
+  r.counts = counts;
+  r.offsets = offsets;
+  r.perm = perm;
+  r.inv = inv;
+  r.bad = reinterpret_cast<int32_t*>(ws + L.bad);
+  MOE_HIP_CHECK(launch_route(r, s));
+  if (p->flags & MOE_FLAG_CHECK_INDICES) {
+    int32_t bad = 0;
+    MOE_HIP_CHECK(hipMemcpyAsync(&bad, r.bad, 4, hipMemcpyDeviceToHost, s));
+    MOE_HIP_CHECK(hipStreamSynchronize(s));
+    if (bad) return MOE_ERR_BAD_INDEX;
+  }
+  return MOE_OK;
+}
+
+moe_status moe_experts_forward(const moe_problem* p, const void* hidden, const int32_t* topk_idx, const float* topk_w,
+                               const void* w_gate_up, const void* w_down, const void* w_gate_up_scale,
+                               const void* w_down_scale, void* out, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  moe_status st = validate_problem(p);
+  if (st != MOE_OK) return st;
+  if (p->T == 0) return MOE_OK;
+  if (!hidden || !topk_idx || !topk_w || !w_gate_up || !w_down || !out || !workspace) return MOE_ERR_NULL_ARG;
+  if (is_fp8(*p) && (!w_gate_up_scale || !w_down_scale)) return MOE_ERR_NULL_ARG;
+  if (!aligned16(hidden) || !aligned16(w_gate_up) || !aligned16(w_down) || !aligned16(out) ||
+      !aligned16(workspace) || !aligned4(topk_idx) || !aligned4(topk_w) || !aligned4(w_gate_up_scale) ||
+      !aligned4(w_down_scale))
+    return MOE_ERR_BAD_SHAPE;
+  const Layout L = make_layout(*p);
+  if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  const Plan pl = make_plan(*p);
+  if (is_fp8(*p) || pl.path == kDecode) {
+    // provided by later kernels; until then only the grouped bf16 / f32 path runs
+    if (is_fp8(*p) || (p->flags & MOE_FLAG_FORCE_DECODE)) return MOE_ERR_UNSUPPORTED;
+  }
+
+  DeviceRecord* dev = nullptr;
+  if ((st = device_record(&dev)) != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const int64_t A = p->T * p->k;
+  const bool det = p->flags & MOE_FLAG_DETERMINISTIC;
+  const bool f32 = p->weight_dtype == MOE_F32;
+
+  int32_t* bad = reinterpret_cast<int32_t*>(ws + L.bad);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  int32_t* mt0 = reinterpret_cast<int32_t*>(ws + L.mt0);
+  int32_t* mt1 = reinterpret_cast<int32_t*>(ws + L.mt1);
+  int32_t* perm = reinterpret_cast<int32_t*>(ws + L.perm);
+  int32_t* inv = reinterpret_cast<int32_t*>(ws + L.inv);
+  float* acc = det ? nullptr : reinterpret_cast<float*>(ws + L.acc);
+  float* slots = det ? reinterpret_cast<float*>(ws + L.slots) : nullptr;
+
+  if (!det) MOE_HIP_CHECK(launch_zero_f32(acc, p->T * (int64_t)p->H, s));
+
+  RouteArgs r{};
+  r.idx = topk_idx;
+  r.A = (int)A;
+  r.E = p->E;
+  r.id_bits = id_bits(p->E);
+  r.counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  r.offsets = offsets;
+  r.perm = perm;
+  r.inv = inv;
+  r.bad = bad;
+  r.bm0 = pl.bm_gu;
+  r.mt0 = mt0;
+  r.bm1 = pl.bm_dn;
+  r.mt1 = mt1;
+  MOE_HIP_CHECK(launch_route(r, s));
+
+  GroupedArgs g{};
+  g.E = p->E;
+  g.offsets = offsets;
+  g.I = p->I;
+  g.H = p->H;
+  g.k = p->k;
+  g.perm = perm;
+  g.topk_w = topk_w;
+  g.acc_out = acc;
+  g.slot_out = slots;
+  void* act = ws + L.act;
+
+  // gate_up + SwiGLU
+  GroupedArgs gu = g;
+  gu.a = hidden;
+  gu.a_rows = perm;
+  gu.a_row_div = p->k;
+  gu.lda = p->H;
+  gu.b = w_gate_up;
+  gu.b_expert_stride = 2 * (int64_t)p->I * p->H;
+  gu.K = p->H;
+  gu.mt = mt0;
+  gu.act_out = act;
+  // down + weight + combine
+  GroupedArgs dn = g;
+  dn.a = act;
+  dn.a_rows = nullptr;
+  dn.a_row_div = 1;
+  dn.lda = p->I;
+  dn.b = w_down;
+  dn.b_expert_stride = (int64_t)p->H * p->I;
+  dn.K = p->I;
+  dn.mt = mt1;
+
+  if (f32) {
+    gu.NT = p->I / 32;
+    dn.NT = p->H / 64;
+    MOE_HIP_CHECK(launch_gateup_f32(gu, max_mtiles(A, p->E, pl.bm_gu) * gu.NT, s));
+    MOE_HIP_CHECK(launch_down_f32(dn, max_mtiles(A, p->E, pl.bm_dn) * dn.NT, s));
+  } else {
+    gu.NT = p->I / 64;
+    dn.NT = p->H / 128;
+    MOE_HIP_CHECK(launch_gateup_bf16(gu, persistent_grid(dev->cus, 2, max_mtiles(A, p->E, pl.bm_gu) * gu.NT), s));
+    MOE_HIP_CHECK(launch_down_bf16(dn, persistent_grid(dev->cus, 2, max_mtiles(A, p->E, pl.bm_dn) * dn.NT), s));
+  }
+
+  const int out_bf16 = p->act_dtype == MOE_BF16;
+  if (det) MOE_HIP_CHECK(launch_finalize_slots(slots, inv, out, p->T, p->k, p->H, out_bf16, s));
+  else MOE_HIP_CHECK(launch_finalize_acc(acc, out, p->T, p->H, out_bf16, s));
+
+  if (p->flags & MOE_FLAG_CHECK_INDICES) {
+    int32_t nbad = 0;
+    MOE_HIP_CHECK(hipMemcpyAsync(&nbad, bad, 4, hipMemcpyDeviceToHost, s));
+    MOE_HIP_CHECK(hipStreamSynchronize(s));
+    if (nbad) return MOE_ERR_BAD_INDEX;
+  }
+  return MOE_OK;
+}
+
+moe_status moe_quantize_rows_fp8(const void* x_bf16, int64_t rows, int32_t cols, uint8_t* q, float* scales,
+                                 void* stream) {
+  if (rows < 0 || cols <= 0 || cols % 128 != 0) return MOE_ERR_BAD_SHAPE;
+  if (rows == 0) return MOE_OK;
+  if (!x_bf16 || !q || !scales) return MOE_ERR_NULL_ARG;
+  (void)stream;
+  return MOE_ERR_UNSUPPORTED;
+}
+
+}  // extern "C"

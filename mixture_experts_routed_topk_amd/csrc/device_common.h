@@ -1,0 +1,86 @@
+// Device-side helpers shared by the HIP kernels of the experts forward (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------- bf16
+
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// float -> bf16 bits, round to nearest even; NaN -> canonical quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// ---------------------------------------------------------------------------- e4m3
+// OCP E4M3 ("e4m3fn"): bias 7, 3 fraction bits, subnormal quantum 2^-9, largest
+// finite 448 (0x7E), 0x7F NaN, no infinity.  Round to nearest even, saturating.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return 0x7fu;                  // NaN
+  if (a >= 0x43e80000u) return sign | 0x7eu;          // |v| >= 464 (or inf): saturate
+  if (a < 0x3c800000u) {                              // |v| < 2^-6: subnormal range
+    const float f = __uint_as_float(a) * 512.0f;      // exact power-of-two scaling
+    return sign | (uint32_t)__builtin_rintf(f);       // 0..8 (8 is the smallest normal)
+  }
+  const uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u); // RNE at fraction bit 20
+  const uint32_t e = (r >> 23) - 127u + 7u;           // biased e4m3 exponent, 1..15
+  return sign | (e << 3) | ((r >> 20) & 7u);
+}
+
+// ---------------------------------------------------------------------------- math
+
+__device__ __forceinline__ float silu_fast(float z) { return z / (1.0f + __expf(-z)); }
+__device__ __forceinline__ float silu_exact(float z) { return z / (1.0f + expf(-z)); }
+
+// ---------------------------------------------------------------------------- MFMA
+
+// C[16x16] += A[16x32] * B[32x16]; lane l holds A row (l & 15) and B column (l & 15),
+// eight consecutive k of group (l >> 4); C: column (l & 15), rows 4*(l >> 4) + i.
+__device__ __forceinline__ f32x4 mfma_16x16x32_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// C[16x16] += A[16x128] * B[128x16] with e4m3 operands (32 bytes per lane), unit
+// block scales (E8M0 exponent 127 = 2^0 on both sides).
+__device__ __forceinline__ f32x4 mfma_16x16x128_e4m3(i32x8 a, i32x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// ---------------------------------------------------------------------------- misc
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Largest e in [0, E) with start[e] * nt <= w (start is non-decreasing, start[E] * nt > w).
+__device__ __forceinline__ int find_group(const int32_t* __restrict__ start, int E, int nt, int w) {
+  int lo = 0, hi = E - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (start[mid] * nt <= w) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+}  // namespace moe

@@ -1,0 +1,83 @@
+// Internal launch interfaces between the C ABI layer (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---------------------------------------------------------------------------- routing
+struct RouteArgs {
+  const int32_t* idx;  // [A] flattened topk_idx
+  int A;
+  int E;
+  int id_bits;         // bits needed for ids in [0, E)
+  int32_t* counts;     // [E] (may be null)
+  int32_t* offsets;    // [E+1]
+  int32_t* perm;       // [A]
+  int32_t* inv;        // [A] (may be null)
+  int32_t* bad;        // [1] out-of-range ids (may be null)
+  int bm0;             // tile height of table mt0 (0 = none)
+  int32_t* mt0;        // [E+1]
+  int bm1;
+  int32_t* mt1;
+};
+size_t route_lds_bytes(int E);
+hipError_t launch_route(const RouteArgs& args, hipStream_t stream);
+
+// ---------------------------------------------------------------------------- grouped GEMMs
+// Common description of one grouped GEMM over expert-sorted rows.
+struct GroupedArgs {
+  // A operand: row p of the sorted order reads source row src(p) of `a`,
+  // src(p) = a_rows ? a_rows[p] / a_row_div : p
+  const void* a;
+  const int32_t* a_rows;
+  int a_row_div;
+  int64_t lda;              // elements per source row
+  const float* a_scale;     // fp8 only: [rows][K/128] float32 scales of `a`
+  // B operand: weights [E][n_total][K]
+  const void* b;
+  int64_t b_expert_stride;  // elements
+  const void* b_scale;      // fp8 only: [E][n_total/128][K/128] float32 or uint8 (UE8M0)
+  int b_scale_ue8m0;
+  int K;
+  int E;
+  int NT;                   // number of N tiles
+  const int32_t* offsets;   // [E+1] sorted-row offsets per expert
+  const int32_t* mt;        // [E+1] M-tile starts for this GEMM's tile height
+  // gate_up epilogue
+  int I;                    // intermediate size (up rows start at I)
+  void* act_out;            // [A][I] SwiGLU output (bf16 / f32)
+  // down epilogue
+  const int32_t* perm;      // sorted position -> slot
+  const float* topk_w;      // [A] routing weights by slot
+  int k;
+  int H;
+  float* acc_out;           // [T][H] float32 accumulator (atomic combine), or
+  float* slot_out;          // [A][H] float32 per-slot rows (deterministic combine)
+};
+
+// Upper bound on M tiles for a tile height (host-side grid sizing).
+inline int64_t max_mtiles(int64_t A, int E, int bm) { return A / bm + (A < E ? A : E); }
+
+int gateup_bf16_bm();
+int down_bf16_bm();
+hipError_t launch_gateup_bf16(const GroupedArgs& g, int grid, hipStream_t s);
+hipError_t launch_down_bf16(const GroupedArgs& g, int grid, hipStream_t s);
+
+int gateup_f32_bm();
+int down_f32_bm();
+hipError_t launch_gateup_f32(const GroupedArgs& g, int64_t max_items, hipStream_t s);
+hipError_t launch_down_f32(const GroupedArgs& g, int64_t max_items, hipStream_t s);
+
+// ---------------------------------------------------------------------------- elementwise
+hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);
+// out[t][h] = round(acc[t][h]) (out_bf16 != 0: bf16 RNE, else float32 copy)
+hipError_t launch_finalize_acc(const float* acc, void* out, int64_t T, int H, int out_bf16,
+                               hipStream_t s);
+// out[t][h] = round(sum_j slot_rows[t*k + j][h]) over slots with inv != -1, in slot order
+hipError_t launch_finalize_slots(const float* slot_rows, const int32_t* inv, void* out, int64_t T,
+                                 int k, int H, int out_bf16, hipStream_t s);
+
+}  // namespace moe

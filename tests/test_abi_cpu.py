@@ -1,0 +1,137 @@
+"""The C-ABI library loads without a GPU, exports what the header declares, and
+rejects bad arguments on the host before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_routed_topk_amd as m
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_experts.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert _declared() == sorted(m.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = m.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+    assert L.moe_abi_version() == 1
+    for s in range(7):
+        assert L.moe_status_str(s)
+
+
+def P(**kw):
+    d = dict(T=32, H=128, I=256, E=8, k=2, act=m.F32, weight=m.F32, scale=m.SCALE_NONE, flags=0)
+    d.update(kw)
+    return m.Problem(d["T"], d["H"], d["I"], d["E"], d["k"], d["act"], d["weight"], d["scale"],
+                     d["flags"])
+
+
+def _ws(p):
+    n = ctypes.c_size_t(0)
+    return m.lib().moe_workspace_size(ctypes.byref(p), ctypes.byref(n)), n.value
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), m.OK),
+    (dict(act=m.BF16, weight=m.BF16), m.OK),
+    (dict(act=m.BF16, weight=m.FP8_E4M3, scale=m.SCALE_F32), m.OK),
+    (dict(act=m.BF16, weight=m.FP8_E4M3, scale=m.SCALE_UE8M0), m.OK),
+    (dict(T=0), m.OK),
+    (dict(k=9), m.ERR_BAD_SHAPE),
+    (dict(k=0), m.ERR_BAD_SHAPE),
+    (dict(E=0), m.ERR_BAD_SHAPE),
+    (dict(E=1025, k=1), m.ERR_BAD_SHAPE),
+    (dict(T=-1), m.ERR_BAD_SHAPE),
+    (dict(H=96), m.ERR_BAD_SHAPE),
+    (dict(I=96), m.ERR_BAD_SHAPE),
+    (dict(act=m.BF16, weight=m.FP8_E4M3, scale=m.SCALE_F32, I=192), m.ERR_BAD_SHAPE),
+    (dict(T=2**30, k=2), m.ERR_BAD_SHAPE),
+    (dict(act=m.F32, weight=m.BF16), m.ERR_UNSUPPORTED),
+    (dict(act=m.BF16, weight=m.FP8_E4M3), m.ERR_UNSUPPORTED),          # fp8 without scales
+    (dict(act=m.BF16, weight=m.BF16, scale=m.SCALE_F32), m.ERR_UNSUPPORTED),
+    (dict(act=m.F32, weight=m.FP8_E4M3, scale=m.SCALE_F32), m.ERR_UNSUPPORTED),
+    (dict(flags=m.FLAG_FORCE_DECODE | m.FLAG_FORCE_GROUPED), m.ERR_UNSUPPORTED),
+    (dict(flags=64), m.ERR_UNSUPPORTED),
+])
+def test_problem_validation(kw, status):
+    st, n = _ws(P(**kw))
+    assert st == status
+    if status == m.OK:
+        assert n > 0
+
+
+def test_workspace_grows_with_deterministic():
+    p = P(act=m.BF16, weight=m.BF16, T=4096, H=2048, I=1408, E=60, k=4)
+    _, n0 = _ws(p)
+    p.flags = m.FLAG_DETERMINISTIC
+    _, n1 = _ws(p)
+    assert n1 - n0 >= 4 * 4096 * 4 * 2048 - 4 * 4096 * 2048
+
+
+def test_forward_rejects_before_any_hip_call():
+    L = m.lib()
+    p = P()
+    fake = ctypes.c_void_p(0x10000)  # never dereferenced: validation fails first
+    # null hidden
+    st = L.moe_experts_forward(ctypes.byref(p), None, fake, fake, fake, fake, None, None, fake,
+                               fake, 1 << 40, None)
+    assert st == m.ERR_NULL_ARG
+    # workspace too small
+    st = L.moe_experts_forward(ctypes.byref(p), fake, fake, fake, fake, fake, None, None, fake,
+                               fake, 16, None)
+    assert st == m.ERR_WORKSPACE
+    # misaligned hidden
+    st = L.moe_experts_forward(ctypes.byref(p), ctypes.c_void_p(0x10004), fake, fake, fake, fake,
+                               None, None, fake, fake, 1 << 40, None)
+    assert st == m.ERR_BAD_SHAPE
+    # fp8 without scale pointers
+    p8 = P(act=m.BF16, weight=m.FP8_E4M3, scale=m.SCALE_F32)
+    st = L.moe_experts_forward(ctypes.byref(p8), fake, fake, fake, fake, fake, None, None, fake,
+                               fake, 1 << 40, None)
+    assert st == m.ERR_NULL_ARG
+    # null problem
+    assert L.moe_experts_forward(None, fake, fake, fake, fake, fake, None, None, fake, fake,
+                                 1 << 40, None) == m.ERR_NULL_ARG
+    # T == 0 is a no-op that touches nothing
+    p0 = P(T=0)
+    assert L.moe_experts_forward(ctypes.byref(p0), None, None, None, None, None, None, None, None,
+                                 None, 0, None) == m.OK
+
+
+def test_quantize_rows_validation():
+    L = m.lib()
+    fake = ctypes.c_void_p(0x10000)
+    assert L.moe_quantize_rows_fp8(fake, 4, 100, fake, fake, None) == m.ERR_BAD_SHAPE
+    assert L.moe_quantize_rows_fp8(fake, -1, 128, fake, fake, None) == m.ERR_BAD_SHAPE
+    assert L.moe_quantize_rows_fp8(None, 4, 128, fake, fake, None) == m.ERR_NULL_ARG
+    assert L.moe_quantize_rows_fp8(None, 0, 128, None, None, None) == m.OK
+
+
+def test_plan_describe():
+    s = m.plan_describe(P(act=m.BF16, weight=m.BF16, T=4096, H=2048, I=1408, E=60, k=4))
+    assert "path=grouped" in s and "weights=bf16" in s
+    s = m.plan_describe(P(act=m.BF16, weight=m.BF16, T=16, H=2048, I=1408, E=60, k=4))
+    assert "path=decode" in s
+    s = m.plan_describe(P(act=m.BF16, weight=m.BF16, T=16, H=2048, I=1408, E=60, k=4,
+                          flags=m.FLAG_FORCE_GROUPED))
+    assert "path=grouped" in s
+
+
+def test_python_wrapper_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 128)
+    with pytest.raises(ValueError):
+        m.experts_forward(x, torch.zeros(4, 2, dtype=torch.int32), torch.zeros(4, 2),
+                          torch.zeros(8, 512, 128), torch.zeros(8, 128, 256))
