@@ -1,0 +1,282 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed top-k experts forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+
+One step is one full forward -- routing bookkeeping, (fp8: activation
+quantisation,) gate/up GEMM + SwiGLU, down GEMM + weighted combine, finalize --
+over one batch of seeded synthetic inputs already resident in HBM.  The default
+workload is the Qwen1.5-MoE-A2.7B-shaped bf16 prefill layer (T=4096, H=2048,
+I=1408, E=60, top-4).  Prints one JSON line: whole-job tokens/s, the dominant
+kernel's roofline figures (its launches timed with HIP events on the library's
+stream inside the timed region), and the CPU oracle timed on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0                                            # MI355X HBM3E, GB/s
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}      # dense, TFLOP/s
+
+WORKLOADS = {
+    "tiny_fp32": "tiny fp32 MoE layer: T=32 H=128 I=256 E=8 top-2, renormalised",
+    "qwen_prefill_bf16": "Qwen1.5-MoE-A2.7B-shaped bf16 prefill: T=4096 H=2048 I=1408 E=60 top-4",
+    "qwen_decode_bf16": "Qwen1.5-MoE-A2.7B-shaped bf16 decode: T=16 H=2048 I=1408 E=60 top-4",
+    "dsv3_prefill_bf16": "DeepSeek-V3-shaped bf16 prefill, Zipf-skewed routing: T=8192 H=7168 I=2048 E=256 top-8",
+    "dsv3_fp8_f32scale": "DeepSeek-V3-shaped fp8-e4m3 experts, 128x128 float32 block scales: T=4096 H=7168 I=2048 E=256 top-8",
+    "dsv3_fp8_ue8m0": "DeepSeek-V3-shaped fp8-e4m3 experts, 128x128 UE8M0 block scales: T=4096 H=7168 I=2048 E=256 top-8",
+}
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime already loaded by torch."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            ev = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(ev.value)
+        return out
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        self.hip.hipEventSynchronize(ctypes.c_void_p(b))
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            self.hip.hipGetLastError()  # an event of a stage the path does not run: clear the error
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def algorithmic(spec, active_count, stage):
+    """(flops, bytes) the method must do/move in one launch of a stage."""
+    A, H, I = spec.A, spec.H, spec.I
+    wb = {"f32": 4, "bf16": 2, "fp8": 1}[spec.weight]
+    xb = {"f32": 4, "bf16": 2}[spec.act]
+    ab = {"f32": 4, "bf16": 2, "fp8": 1}[spec.weight]          # SwiGLU rows as stored
+    sb = 0
+    if spec.weight == "fp8":
+        sb = 4 if spec.scale == "f32" else 1
+    if stage == "gate_up":
+        flops = 4.0 * A * H * I
+        byts = active_count * (2 * I * H * wb + (2 * I // 128) * (H // 128) * sb)
+        byts += spec.T * H * (1 if spec.weight == "fp8" else xb) + A * I * ab
+        if spec.weight == "fp8":
+            byts += spec.T * (H // 128) * 4 + A * (I // 128) * 4
+    elif stage == "down":
+        flops = 2.0 * A * H * I
+        byts = active_count * (H * I * wb + (H // 128) * (I // 128) * sb)
+        byts += A * I * ab + spec.T * H * 4
+        if spec.weight == "fp8":
+            byts += A * (I // 128) * 4
+    else:
+        raise ValueError(stage)
+    return flops, float(byts)
+
+
+def layer_totals(spec, active_count):
+    """Whole-layer algorithmic flops and bytes (active expert weights + x + out + routing)."""
+    wb = {"f32": 4, "bf16": 2, "fp8": 1}[spec.weight]
+    xb = {"f32": 4, "bf16": 2}[spec.act]
+    flops = 6.0 * spec.A * spec.H * spec.I
+    byts = active_count * 3 * spec.I * spec.H * wb + 2 * spec.T * spec.H * xb + 8 * spec.A
+    if spec.weight == "fp8":
+        sb = 4 if spec.scale == "f32" else 1
+        byts += active_count * 3 * (spec.I // 128) * (spec.H // 128) * sb
+    return flops, float(byts)
+
+
+def cpu_baseline(spec, D, seconds: float):
+    """The fp64 oracle (per-token loop over the k chosen experts) on a token sample."""
+    import numpy as np
+    import synth
+    from oracle.moe import ExpertWeights, forward
+
+    cache = {}
+
+    def get(which, e):
+        key = (which, e)
+        if key not in cache:
+            cache[key] = (synth.expert_gate_up if which == 0 else synth.expert_down)(spec, e)
+        return cache[key]
+
+    if spec.weight == "fp8":
+        W = ExpertWeights("fp8", lambda e: get(0, e)[0], lambda e: get(1, e)[0], spec.scale,
+                          lambda e: get(0, e)[1], lambda e: get(1, e)[1])
+    else:
+        W = ExpertWeights(spec.weight, lambda e: get(0, e), lambda e: get(1, e))
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    # warm the weight cache for the first tokens so generation is not timed
+    n_done, t_oracle = 0, 0.0
+    t = 0
+    while t_oracle < seconds and t < spec.T:
+        for e in set(int(v) for v in D["idx_host"][t]):
+            get(0, e), get(1, e)
+        t0 = time.perf_counter()
+        forward(D["x_host"], D["idx_host"], D["w_host"], W, act=spec.act, E=spec.E,
+                mode="literal", tokens=[t])
+        t_oracle += time.perf_counter() - t0
+        n_done += 1
+        t += 1
+    return {"value": n_done / t_oracle, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n_done} tokens of the same layer, fp64 per-token loop over the k "
+                      f"chosen experts (literal mode), {t_oracle:.1f} s of CPU time",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="qwen_prefill_bf16", choices=sorted(WORKLOADS))
+    ap.add_argument("--flags", type=int, default=0, help="MOE_FLAG_* bits passed to the forward")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this experts forward is a single-GPU library "
+              "(no sharding, no collectives); run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mixture_experts_routed_topk_amd as m
+    import synth
+    from synth.device import device_layer
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    spec = synth.spec_for(args.config)
+    D = device_layer(spec, dev)
+    n_active = len(D["active"])
+    kw = {}
+    if spec.weight == "fp8":
+        kw = dict(w_gate_up_scale=D["w_gate_up_scale"], w_down_scale=D["w_down_scale"])
+    prob = m.problem_for(D["x"], D["idx"], D["w_gate_up"], D["w_down"], kw.get("w_gate_up_scale"),
+                         args.flags)
+    ws = torch.empty(m.workspace_size(prob), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(D["x"])
+    plan = m.plan_describe(prob)
+
+    def step():
+        m.experts_forward(D["x"], D["idx"], D["w"], D["w_gate_up"], D["w_down"], out=out,
+                          flags=args.flags, workspace=ws, **kw)
+
+    hev = HipEvents()
+    nst = len(m.STAGES)
+    # warm-up, with every stage bracketed by events to find the dominant kernel
+    warm = max(args.warmup, 1)
+    wev = hev.create(2 * nst * warm)
+    for i in range(warm):
+        m.set_stage_events(wev[2 * nst * i: 2 * nst * (i + 1)])
+        step()
+    m.set_stage_events(None)
+    torch.cuda.synchronize()
+    stage_ms = {}
+    for s, name in enumerate(m.STAGES):
+        vals = []
+        for i in range(warm):
+            a, b = wev[2 * nst * i + 2 * s], wev[2 * nst * i + 2 * s + 1]
+            try:
+                vals.append(hev.elapsed_ms(a, b))
+            except RuntimeError:
+                vals = []
+                break
+        if vals:
+            stage_ms[name] = sorted(vals)[len(vals) // 2]
+    hev.destroy(wev)
+    dominant = max(("gate_up", "down"), key=lambda n: stage_ms.get(n, 0.0))
+    dom = m.STAGES.index(dominant)
+
+    # timed region: only the dominant kernel is bracketed by events
+    tev = hev.create(2 * args.steps)
+    handles = [None] * (2 * nst)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        handles[2 * dom], handles[2 * dom + 1] = tev[2 * i], tev[2 * i + 1]
+        m.set_stage_events(handles)
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    m.set_stage_events(None)
+    kern_ms = [hev.elapsed_ms(tev[2 * i], tev[2 * i + 1]) for i in range(args.steps)]
+    hev.destroy(tev)
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    tokens_per_s = spec.T * args.steps / (t1 - t0)
+    kavg = sum(kern_ms) / len(kern_ms)
+    flops, byts = algorithmic(spec, n_active, dominant)
+    peak_f = PEAK_TFLOPS[spec.weight]
+    t_mfma = flops / (peak_f * 1e12)
+    t_hbm = byts / (PEAK_HBM_GBS * 1e9)
+    if t_mfma >= t_hbm:
+        roof = {"bound": "mfma", "achieved": flops / (kavg * 1e-3) / 1e12, "peak": peak_f, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": byts / (kavg * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof.update({"kernel": dominant, "avg_ms": kavg, "launches": len(kern_ms),
+                 "algorithmic_flops": flops, "algorithmic_bytes": byts,
+                 "mfma_frac": flops / (kavg * 1e-3) / 1e12 / peak_f,
+                 "hbm_frac": byts / (kavg * 1e-3) / 1e9 / PEAK_HBM_GBS})
+    lf, lb = layer_totals(spec, n_active)
+    sec = ms_per_step * 1e-3
+    res = {
+        "metric": "MoE-layer tokens/s + achieved TFLOP/s (prefill) / HBM GB/s (decode)",
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.weight,
+        "data": "synthetic (seeded random weights and routing; no checkpoint)",
+        "config": {"workload": WORKLOADS[args.config], "name": args.config, "T": spec.T, "H": spec.H,
+                   "I": spec.I, "E": spec.E, "k": spec.k, "active_experts": n_active,
+                   "routing": spec.routing, "scales": spec.scale, "plan": plan, "flags": args.flags},
+        "tflops": lf / sec / 1e12,
+        "hbm_gbps": lb / sec / 1e9,
+        "layer_mfma_frac": lf / sec / 1e12 / peak_f,
+        "layer_hbm_frac": lb / sec / 1e9 / PEAK_HBM_GBS,
+        "stages_ms": stage_ms,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(spec, D, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

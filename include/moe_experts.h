@@ -172,6 +172,28 @@ moe_status moe_quantize_rows_fp8(const void* x_bf16, int64_t rows, int32_t cols,
  * terminated, truncated to len).  Host only. */
 moe_status moe_plan_describe(const moe_problem* p, char* buf, size_t len);
 
+/* Stages of one forward, in launch order (a stage a path does not use is skipped). */
+enum {
+  MOE_STAGE_ZERO = 0,      /* clear the float32 accumulator                      */
+  MOE_STAGE_ROUTE = 1,     /* routing bookkeeping                                */
+  MOE_STAGE_QUANT_X = 2,   /* fp8 only: quantise the hidden states               */
+  MOE_STAGE_GATE_UP = 3,   /* gate/up projection + SwiGLU                        */
+  MOE_STAGE_QUANT_ACT = 4, /* fp8 only: quantise the SwiGLU output               */
+  MOE_STAGE_DOWN = 5,      /* down projection + routing weight + combine         */
+  MOE_STAGE_FINALIZE = 6,  /* round the accumulator to the output type           */
+  MOE_STAGE_COUNT = 7
+};
+
+/*
+ * Per-stage timing hook for profilers and benchmarks.  `events` points to
+ * 2 * MOE_STAGE_COUNT hipEvent_t handles (entries may be NULL); while set, each
+ * later moe_experts_forward on the calling host thread records events[2*s] on its
+ * stream just before stage s and events[2*s+1] just after it.  The handles are
+ * copied; the caller keeps ownership of the events.  events == NULL (or n == 0)
+ * clears the hook.  n must be 0 or 2 * MOE_STAGE_COUNT (else MOE_ERR_BAD_SHAPE).
+ */
+moe_status moe_set_stage_events(void* const* events, int n);
+
 #ifdef __cplusplus
 }
 #endif

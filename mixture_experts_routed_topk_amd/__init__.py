@@ -36,7 +36,10 @@ FLAG_FORCE_GROUPED = 4
 FLAG_FORCE_DECODE = 8
 
 EXPORTS = ["moe_abi_version", "moe_status_str", "moe_workspace_size", "moe_experts_forward",
-           "moe_route", "moe_quantize_rows_fp8", "moe_plan_describe"]
+           "moe_route", "moe_quantize_rows_fp8", "moe_plan_describe", "moe_set_stage_events"]
+
+# stage ids (moe_set_stage_events)
+STAGES = ["zero", "route", "quant_x", "gate_up", "quant_act", "down", "finalize"]
 
 
 class Problem(ctypes.Structure):
@@ -80,6 +83,8 @@ def lib():
     L.moe_quantize_rows_fp8.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, vp, vp, vp]
     L.moe_plan_describe.restype = ctypes.c_int
     L.moe_plan_describe.argtypes = [P, ctypes.c_char_p, sz]
+    L.moe_set_stage_events.restype = ctypes.c_int
+    L.moe_set_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
     _lib = L
     return L
 
@@ -210,6 +215,16 @@ def route(topk_idx: torch.Tensor, E: int, flags: int = 0, workspace=None):
     _check(lib().moe_route(ctypes.byref(prob), _ptr(topk_idx), _ptr(counts), _ptr(offsets),
                            _ptr(perm), _ptr(inv), _ptr(workspace), workspace.numel(), _stream(dev)))
     return counts, offsets, perm[: T * k], inv[: T * k]
+
+
+def set_stage_events(handles):
+    """Install per-stage hipEvent_t handles (a list of 2*len(STAGES) ints or None) on this thread;
+    None clears the hook."""
+    if handles is None:
+        _check(lib().moe_set_stage_events(None, 0))
+        return
+    arr = (ctypes.c_void_p * len(handles))(*[h or None for h in handles])
+    _check(lib().moe_set_stage_events(arr, len(handles)))
 
 
 def quantize_rows_fp8(x: torch.Tensor):

@@ -60,35 +60,38 @@ enum Path { kGrouped = 0, kDecode = 1 };
 
 struct Plan {
   Path path;
-  int bm_gu, bm_dn;  // grouped tile heights
+  int bm;  // row-group height of the tile table the GEMMs walk
 };
+
+bool decode_capable(const moe_problem& p) { return p.weight_dtype == MOE_BF16 && p.I % 128 == 0; }
 
 Plan make_plan(const moe_problem& p) {
   Plan pl;
   bool decode = p.T <= kDecodeMaxTokens;
   if (p.flags & MOE_FLAG_FORCE_GROUPED) decode = false;
   if (p.flags & MOE_FLAG_FORCE_DECODE) decode = true;
+  if (!decode_capable(p)) decode = false;
   pl.path = decode ? kDecode : kGrouped;
-  if (p.weight_dtype == MOE_F32) {
-    pl.bm_gu = gateup_f32_bm();
-    pl.bm_dn = down_f32_bm();
-  } else {
-    pl.bm_gu = gateup_bf16_bm();
-    pl.bm_dn = down_bf16_bm();
-  }
+  if (decode) pl.bm = decode_bm();
+  else pl.bm = p.weight_dtype == MOE_F32 ? gateup_f32_bm() : grouped_mfma_bm();
   return pl;
 }
 
 // ---------------------------------------------------------------------------- workspace
 
 struct Layout {
-  size_t bad, counts, offsets, mt0, mt1, perm, inv, act, acc, slots, total;
+  size_t bad, counts, offsets, mt, perm, inv;
+  size_t act;        // SwiGLU rows [A][I]: f32 (f32 weights, and fp8 before quantising) or bf16
+  size_t act_q;      // fp8: e4m3 SwiGLU rows [A][I]
+  size_t act_s;      // fp8: their scales [A][I/128]
+  size_t x_q, x_s;   // fp8: e4m3 hidden rows [T][H] and scales [T][H/128]
+  size_t acc, slots, total;
 };
 
 size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
 
 Layout make_layout(const moe_problem& p) {
-  const size_t A = (size_t)p.T * p.k, E = p.E;
+  const size_t A = (size_t)p.T * p.k, E = p.E, T = (size_t)p.T, H = p.H, I = p.I;
   Layout L;
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -99,15 +102,18 @@ Layout make_layout(const moe_problem& p) {
   L.bad = take(4);
   L.counts = take(4 * E);
   L.offsets = take(4 * (E + 1));
-  L.mt0 = take(4 * (E + 1));
-  L.mt1 = take(4 * (E + 1));
+  L.mt = take(4 * (E + 1));
   L.perm = take(4 * A);
   L.inv = take(4 * A);
-  const size_t act_elem = p.weight_dtype == MOE_F32 ? 4 : 2;
-  L.act = take(act_elem * A * p.I);
+  const bool fp8 = p.weight_dtype == MOE_FP8_E4M3;
+  L.act = take((p.weight_dtype == MOE_BF16 ? 2 : 4) * A * I);
+  L.act_q = fp8 ? take(A * I) : o;
+  L.act_s = fp8 ? take(4 * A * (I / 128)) : o;
+  L.x_q = fp8 ? take(T * H) : o;
+  L.x_s = fp8 ? take(4 * T * (H / 128)) : o;
   const bool det = p.flags & MOE_FLAG_DETERMINISTIC;
-  L.acc = det ? o : take(4 * (size_t)p.T * p.H);
-  L.slots = det ? take(4 * A * p.H) : o;
+  L.acc = det ? o : take(4 * T * H);
+  L.slots = det ? take(4 * A * H) : o;
   L.total = o;
   return L;
 }
@@ -141,6 +147,16 @@ int persistent_grid(int cus, int per_cu, int64_t max_items) {
   if (max_items < g) g = max_items;
   g = (g + 7) / 8 * 8;
   return (int)(g < 8 ? 8 : g);
+}
+
+// per-thread stage-event hook (moe_set_stage_events)
+thread_local hipEvent_t t_stage_events[2 * MOE_STAGE_COUNT] = {};
+thread_local bool t_stage_hook = false;
+
+hipError_t stage_mark(int stage, int edge, hipStream_t s) {
+  if (!t_stage_hook) return hipSuccess;
+  hipEvent_t ev = t_stage_events[2 * stage + edge];
+  return ev ? hipEventRecord(ev, s) : hipSuccess;
 }
 
 #define MOE_HIP_CHECK(expr)                  \
@@ -186,10 +202,11 @@ moe_status moe_plan_describe(const moe_problem* p, char* buf, size_t len) {
   const Layout L = make_layout(*p);
   const char* wname = p->weight_dtype == MOE_F32 ? "f32" : (p->weight_dtype == MOE_BF16 ? "bf16" : "fp8_e4m3");
   const char* sname = p->scale_fmt == MOE_SCALE_F32 ? "f32" : (p->scale_fmt == MOE_SCALE_UE8M0 ? "ue8m0" : "none");
-  snprintf(buf, len,
-           "path=%s weights=%s scales=%s gate_up_tile=%dx%d down_tile=%dx%d combine=%s workspace_bytes=%zu",
-           pl.path == kDecode ? "decode" : "grouped", wname, sname, pl.bm_gu,
-           p->weight_dtype == MOE_F32 ? 64 : 128, pl.bm_dn, p->weight_dtype == MOE_F32 ? 64 : 128,
+  const char* kern = pl.path == kDecode ? "stream_weights_16tok_mfma16x16x32"
+                     : p->weight_dtype == MOE_F32 ? "fma_64x64"
+                     : p->weight_dtype == MOE_BF16 ? "mfma16x16x32_bf16_128x128" : "mfma16x16x128_e4m3_128x128";
+  snprintf(buf, len, "path=%s weights=%s scales=%s kernels=%s combine=%s workspace_bytes=%zu",
+           pl.path == kDecode ? "decode" : "grouped", wname, sname, kern,
            (p->flags & MOE_FLAG_DETERMINISTIC) ? "slot_rows" : "atomic_f32", L.total);
   return MOE_OK;
 }
@@ -207,6 +224,7 @@ moe_status moe_route(const moe_problem* p, const int32_t* topk_idx, int32_t* cou
   if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
   DeviceRecord* dev = nullptr;
   if ((st = device_record(&dev)) != MOE_OK) return st;
+  (void)hipGetLastError();  // see moe_experts_forward
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   RouteArgs r{};
@@ -237,21 +255,22 @@ moe_status moe_experts_forward(const moe_problem* p, const void* hidden, const i
   if (st != MOE_OK) return st;
   if (p->T == 0) return MOE_OK;
   if (!hidden || !topk_idx || !topk_w || !w_gate_up || !w_down || !out || !workspace) return MOE_ERR_NULL_ARG;
-  if (is_fp8(*p) && (!w_gate_up_scale || !w_down_scale)) return MOE_ERR_NULL_ARG;
+  const bool fp8 = is_fp8(*p);
+  if (fp8 && (!w_gate_up_scale || !w_down_scale)) return MOE_ERR_NULL_ARG;
   if (!aligned16(hidden) || !aligned16(w_gate_up) || !aligned16(w_down) || !aligned16(out) ||
       !aligned16(workspace) || !aligned4(topk_idx) || !aligned4(topk_w) || !aligned4(w_gate_up_scale) ||
       !aligned4(w_down_scale))
     return MOE_ERR_BAD_SHAPE;
   const Layout L = make_layout(*p);
   if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if ((p->flags & MOE_FLAG_FORCE_DECODE) && !decode_capable(*p)) return MOE_ERR_UNSUPPORTED;
   const Plan pl = make_plan(*p);
-  if (is_fp8(*p) || pl.path == kDecode) {
-    // provided by later kernels; until then only the grouped bf16 / f32 path runs
-    if (is_fp8(*p) || (p->flags & MOE_FLAG_FORCE_DECODE)) return MOE_ERR_UNSUPPORTED;
-  }
 
   DeviceRecord* dev = nullptr;
   if ((st = device_record(&dev)) != MOE_OK) return st;
+  // launch errors are read with hipGetLastError(); drop an error left behind by an
+  // earlier, unrelated HIP call on this thread so it is not reported as ours
+  (void)hipGetLastError();
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   const int64_t A = p->T * p->k;
@@ -260,14 +279,17 @@ moe_status moe_experts_forward(const moe_problem* p, const void* hidden, const i
 
   int32_t* bad = reinterpret_cast<int32_t*>(ws + L.bad);
   int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
-  int32_t* mt0 = reinterpret_cast<int32_t*>(ws + L.mt0);
-  int32_t* mt1 = reinterpret_cast<int32_t*>(ws + L.mt1);
+  int32_t* mt = reinterpret_cast<int32_t*>(ws + L.mt);
   int32_t* perm = reinterpret_cast<int32_t*>(ws + L.perm);
   int32_t* inv = reinterpret_cast<int32_t*>(ws + L.inv);
   float* acc = det ? nullptr : reinterpret_cast<float*>(ws + L.acc);
   float* slots = det ? reinterpret_cast<float*>(ws + L.slots) : nullptr;
 
-  if (!det) MOE_HIP_CHECK(launch_zero_f32(acc, p->T * (int64_t)p->H, s));
+  if (!det) {
+    MOE_HIP_CHECK(stage_mark(MOE_STAGE_ZERO, 0, s));
+    MOE_HIP_CHECK(launch_zero_f32(acc, p->T * (int64_t)p->H, s));
+    MOE_HIP_CHECK(stage_mark(MOE_STAGE_ZERO, 1, s));
+  }
 
   RouteArgs r{};
   r.idx = topk_idx;
@@ -279,15 +301,16 @@ moe_status moe_experts_forward(const moe_problem* p, const void* hidden, const i
   r.perm = perm;
   r.inv = inv;
   r.bad = bad;
-  r.bm0 = pl.bm_gu;
-  r.mt0 = mt0;
-  r.bm1 = pl.bm_dn;
-  r.mt1 = mt1;
+  r.bm0 = pl.bm;
+  r.mt0 = mt;
+  MOE_HIP_CHECK(stage_mark(MOE_STAGE_ROUTE, 0, s));
   MOE_HIP_CHECK(launch_route(r, s));
+  MOE_HIP_CHECK(stage_mark(MOE_STAGE_ROUTE, 1, s));
 
   GroupedArgs g{};
   g.E = p->E;
   g.offsets = offsets;
+  g.mt = mt;
   g.I = p->I;
   g.H = p->H;
   g.k = p->k;
@@ -295,45 +318,83 @@ moe_status moe_experts_forward(const moe_problem* p, const void* hidden, const i
   g.topk_w = topk_w;
   g.acc_out = acc;
   g.slot_out = slots;
-  void* act = ws + L.act;
+  g.b_scale_ue8m0 = p->scale_fmt == MOE_SCALE_UE8M0;
 
-  // gate_up + SwiGLU
+  // gate_up + SwiGLU: rows = hidden rows gathered through perm (token = slot / k)
   GroupedArgs gu = g;
-  gu.a = hidden;
+  gu.a = fp8 ? (const void*)(ws + L.x_q) : hidden;
+  gu.a_scale = fp8 ? reinterpret_cast<const float*>(ws + L.x_s) : nullptr;
   gu.a_rows = perm;
   gu.a_row_div = p->k;
   gu.lda = p->H;
   gu.b = w_gate_up;
+  gu.b_scale = w_gate_up_scale;
+  gu.b_rows = 2 * p->I;
   gu.b_expert_stride = 2 * (int64_t)p->I * p->H;
   gu.K = p->H;
-  gu.mt = mt0;
-  gu.act_out = act;
-  // down + weight + combine
+  gu.act_out = ws + L.act;
+  // down + routing weight + combine: rows = SwiGLU rows in sorted order
   GroupedArgs dn = g;
-  dn.a = act;
+  dn.a = fp8 ? (const void*)(ws + L.act_q) : (const void*)(ws + L.act);
+  dn.a_scale = fp8 ? reinterpret_cast<const float*>(ws + L.act_s) : nullptr;
   dn.a_rows = nullptr;
   dn.a_row_div = 1;
   dn.lda = p->I;
   dn.b = w_down;
+  dn.b_scale = w_down_scale;
+  dn.b_rows = p->H;
   dn.b_expert_stride = (int64_t)p->H * p->I;
   dn.K = p->I;
-  dn.mt = mt1;
 
-  if (f32) {
+  if (fp8) {
+    MOE_HIP_CHECK(stage_mark(MOE_STAGE_QUANT_X, 0, s));
+    MOE_HIP_CHECK(launch_quant_rows_bf16(hidden, p->T, p->H, reinterpret_cast<uint8_t*>(ws + L.x_q),
+                                         reinterpret_cast<float*>(ws + L.x_s), s));
+    MOE_HIP_CHECK(stage_mark(MOE_STAGE_QUANT_X, 1, s));
+  }
+
+  const int64_t active_max = A < p->E ? A : p->E;
+  if (pl.path == kDecode) {
+    gu.NT = p->I / 64;
+    dn.NT = p->H / 64;
+    MOE_HIP_CHECK(stage_mark(MOE_STAGE_GATE_UP, 0, s));
+    MOE_HIP_CHECK(launch_decode_gateup(gu, persistent_grid(dev->cus, 2, active_max * gu.NT), s));
+    MOE_HIP_CHECK(stage_mark(MOE_STAGE_GATE_UP, 1, s));
+    MOE_HIP_CHECK(stage_mark(MOE_STAGE_DOWN, 0, s));
+    MOE_HIP_CHECK(launch_decode_down(dn, persistent_grid(dev->cus, 2, active_max * dn.NT), s));
+    MOE_HIP_CHECK(stage_mark(MOE_STAGE_DOWN, 1, s));
+  } else if (f32) {
     gu.NT = p->I / 32;
     dn.NT = p->H / 64;
-    MOE_HIP_CHECK(launch_gateup_f32(gu, max_mtiles(A, p->E, pl.bm_gu) * gu.NT, s));
-    MOE_HIP_CHECK(launch_down_f32(dn, max_mtiles(A, p->E, pl.bm_dn) * dn.NT, s));
+    MOE_HIP_CHECK(stage_mark(MOE_STAGE_GATE_UP, 0, s));
+    MOE_HIP_CHECK(launch_gateup_f32(gu, max_mtiles(A, p->E, pl.bm) * gu.NT, s));
+    MOE_HIP_CHECK(stage_mark(MOE_STAGE_GATE_UP, 1, s));
+    MOE_HIP_CHECK(stage_mark(MOE_STAGE_DOWN, 0, s));
+    MOE_HIP_CHECK(launch_down_f32(dn, max_mtiles(A, p->E, pl.bm) * dn.NT, s));
+    MOE_HIP_CHECK(stage_mark(MOE_STAGE_DOWN, 1, s));
   } else {
     gu.NT = p->I / 64;
     dn.NT = p->H / 128;
-    MOE_HIP_CHECK(launch_gateup_bf16(gu, persistent_grid(dev->cus, 2, max_mtiles(A, p->E, pl.bm_gu) * gu.NT), s));
-    MOE_HIP_CHECK(launch_down_bf16(dn, persistent_grid(dev->cus, 2, max_mtiles(A, p->E, pl.bm_dn) * dn.NT), s));
+    MOE_HIP_CHECK(stage_mark(MOE_STAGE_GATE_UP, 0, s));
+    MOE_HIP_CHECK(launch_gateup_mfma(gu, fp8, persistent_grid(dev->cus, 2, max_mtiles(A, p->E, pl.bm) * gu.NT), s));
+    MOE_HIP_CHECK(stage_mark(MOE_STAGE_GATE_UP, 1, s));
+    if (fp8) {
+      MOE_HIP_CHECK(stage_mark(MOE_STAGE_QUANT_ACT, 0, s));
+      MOE_HIP_CHECK(launch_quant_rows_f32(reinterpret_cast<const float*>(ws + L.act), A, p->I,
+                                          reinterpret_cast<uint8_t*>(ws + L.act_q),
+                                          reinterpret_cast<float*>(ws + L.act_s), s));
+      MOE_HIP_CHECK(stage_mark(MOE_STAGE_QUANT_ACT, 1, s));
+    }
+    MOE_HIP_CHECK(stage_mark(MOE_STAGE_DOWN, 0, s));
+    MOE_HIP_CHECK(launch_down_mfma(dn, fp8, persistent_grid(dev->cus, 2, max_mtiles(A, p->E, pl.bm) * dn.NT), s));
+    MOE_HIP_CHECK(stage_mark(MOE_STAGE_DOWN, 1, s));
   }
 
   const int out_bf16 = p->act_dtype == MOE_BF16;
+  MOE_HIP_CHECK(stage_mark(MOE_STAGE_FINALIZE, 0, s));
   if (det) MOE_HIP_CHECK(launch_finalize_slots(slots, inv, out, p->T, p->k, p->H, out_bf16, s));
   else MOE_HIP_CHECK(launch_finalize_acc(acc, out, p->T, p->H, out_bf16, s));
+  MOE_HIP_CHECK(stage_mark(MOE_STAGE_FINALIZE, 1, s));
 
   if (p->flags & MOE_FLAG_CHECK_INDICES) {
     int32_t nbad = 0;
@@ -344,13 +405,27 @@ moe_status moe_experts_forward(const moe_problem* p, const void* hidden, const i
   return MOE_OK;
 }
 
+moe_status moe_set_stage_events(void* const* events, int n) {
+  if (events == nullptr || n == 0) {
+    t_stage_hook = false;
+    for (auto& e : t_stage_events) e = nullptr;
+    return MOE_OK;
+  }
+  if (n != 2 * MOE_STAGE_COUNT) return MOE_ERR_BAD_SHAPE;
+  for (int i = 0; i < n; ++i) t_stage_events[i] = static_cast<hipEvent_t>(events[i]);
+  t_stage_hook = true;
+  return MOE_OK;
+}
+
 moe_status moe_quantize_rows_fp8(const void* x_bf16, int64_t rows, int32_t cols, uint8_t* q, float* scales,
                                  void* stream) {
   if (rows < 0 || cols <= 0 || cols % 128 != 0) return MOE_ERR_BAD_SHAPE;
   if (rows == 0) return MOE_OK;
   if (!x_bf16 || !q || !scales) return MOE_ERR_NULL_ARG;
-  (void)stream;
-  return MOE_ERR_UNSUPPORTED;
+  if (!aligned16(x_bf16) || (reinterpret_cast<uintptr_t>(q) & 7u) || !aligned4(scales)) return MOE_ERR_BAD_SHAPE;
+  (void)hipGetLastError();  // see moe_experts_forward
+  MOE_HIP_CHECK(launch_quant_rows_bf16(x_bf16, rows, cols, q, scales, static_cast<hipStream_t>(stream)));
+  return MOE_OK;
 }
 
 }  // extern "C"

@@ -39,8 +39,9 @@ struct GroupedArgs {
   // B operand: weights [E][n_total][K]
   const void* b;
   int64_t b_expert_stride;  // elements
-  const void* b_scale;      // fp8 only: [E][n_total/128][K/128] float32 or uint8 (UE8M0)
+  const void* b_scale;      // fp8 only: [E][b_rows/128][K/128] float32 or uint8 (UE8M0)
   int b_scale_ue8m0;
+  int b_rows;               // rows of one expert's weight matrix (2I or H)
   int K;
   int E;
   int NT;                   // number of N tiles
@@ -61,15 +62,29 @@ struct GroupedArgs {
 // Upper bound on M tiles for a tile height (host-side grid sizing).
 inline int64_t max_mtiles(int64_t A, int E, int bm) { return A / bm + (A < E ? A : E); }
 
-int gateup_bf16_bm();
-int down_bf16_bm();
-hipError_t launch_gateup_bf16(const GroupedArgs& g, int grid, hipStream_t s);
-hipError_t launch_down_bf16(const GroupedArgs& g, int grid, hipStream_t s);
+// bf16 / fp8 MFMA grouped GEMMs (persistent grid)
+int grouped_mfma_bm();
+hipError_t launch_gateup_mfma(const GroupedArgs& g, bool fp8, int grid, hipStream_t s);
+hipError_t launch_down_mfma(const GroupedArgs& g, bool fp8, int grid, hipStream_t s);
 
 int gateup_f32_bm();
 int down_f32_bm();
 hipError_t launch_gateup_f32(const GroupedArgs& g, int64_t max_items, hipStream_t s);
 hipError_t launch_down_f32(const GroupedArgs& g, int64_t max_items, hipStream_t s);
+
+// ---------------------------------------------------------------------------- decode path
+// Small-T path: each active expert's weights are streamed once from HBM against its
+// few rows held in LDS; work items are (expert, 64-column block), persistent grid.
+int decode_bm();
+hipError_t launch_decode_gateup(const GroupedArgs& g, int grid, hipStream_t s);
+hipError_t launch_decode_down(const GroupedArgs& g, int grid, hipStream_t s);
+
+// ---------------------------------------------------------------------------- fp8 rows
+// Per-row, per-128-column e4m3 quantisation: scale = amax/448 (1 if amax == 0).
+hipError_t launch_quant_rows_bf16(const void* x, int64_t rows, int cols, uint8_t* q, float* scales,
+                                  hipStream_t s);
+hipError_t launch_quant_rows_f32(const float* x, int64_t rows, int cols, uint8_t* q, float* scales,
+                                 hipStream_t s);
 
 // ---------------------------------------------------------------------------- elementwise
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);

@@ -18,6 +18,7 @@ namespace {
 
 constexpr int kRouteThreads = 512;
 constexpr int kRouteWaves = kRouteThreads / kWave;
+constexpr int kBatch = 8;             // 64-slot pieces whose ids are loaded together
 
 // Exclusive scan over v[0..n) in LDS (n <= 2 * kRouteThreads); returns the total.
 __device__ int block_exclusive_scan(int32_t* v, int n, int32_t* wave_sums) {
@@ -66,12 +67,22 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs p) {
   const int beg = min(A, wave * per);
   const int end = min(A, beg + per);
 
-  // 1. per-wave histograms
+  // 1. per-wave histograms (ids loaded kBatch pieces at a time to overlap latency)
   int nbad = 0;
-  for (int a = beg + lane; a < end; a += 64) {
-    const int e = p.idx[a];
-    if (e >= 0 && e < E) atomicAdd(&hist[wave * E + e], 1);
-    else ++nbad;
+  for (int a0 = beg; a0 < end; a0 += 64 * kBatch) {
+    int ids[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int a = a0 + 64 * u + lane;
+      ids[u] = a < end ? p.idx[a] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (a0 + 64 * u + lane >= end) continue;
+      const int e = ids[u];
+      if (e >= 0 && e < E) atomicAdd(&hist[wave * E + e], 1);
+      else ++nbad;
+    }
   }
   if (nbad) atomicAdd(&bad, nbad);
   __syncthreads();
@@ -106,7 +117,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs p) {
     __syncthreads();
     for (int e = tid; e < E; e += kRouteThreads) {
       const int c = (e + 1 < E ? offs[e + 1] : valid) - offs[e];
-      tiles[e] = (c + bm - 1) / bm;
+      tiles[e] = c == 0 ? 0 : (c - 1) / bm + 1;
     }
     __syncthreads();
     const int nt = block_exclusive_scan(tiles, E, wave_sums);
@@ -115,33 +126,42 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs p) {
   }
   __syncthreads();
 
-  // 4. stable placement, one 64-slot piece at a time per wave
+  // 4. stable placement, one 64-slot piece at a time per wave (ids batched as above)
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int a0 = beg; a0 < end; a0 += 64) {
-    const int a = a0 + lane;
-    const bool in = a < end;
-    const int e = in ? p.idx[a] : -1;
-    const bool ok = in && e >= 0 && e < E;
-    uint64_t same = __ballot(ok);
-    for (int bit = 0; bit < p.id_bits; ++bit) {
-      const bool set = ok && ((e >> bit) & 1);
-      const uint64_t m = __ballot(set);
-      same &= set ? m : ~m;
+  for (int b0 = beg; b0 < end; b0 += 64 * kBatch) {
+    int ids[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int a = b0 + 64 * u + lane;
+      ids[u] = a < end ? p.idx[a] : -1;
     }
-    if (ok) {
-      const int rank = __popcll(same & below);
-      const int pos = hist[wave * E + e] + rank;
-      p.perm[pos] = a;
-      if (p.inv) p.inv[a] = pos;
-      // the lowest lane of each group advances that expert's cursor; every lane of
-      // the wave has read the cursor above before this store executes
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int a = b0 + 64 * u + lane;
+      const bool in = a < end;
+      const int e = ids[u];
+      const bool ok = in && e >= 0 && e < E;
+      uint64_t same = __ballot(ok);
+      for (int bit = 0; bit < p.id_bits; ++bit) {
+        const bool set = ok && ((e >> bit) & 1);
+        const uint64_t m = __ballot(set);
+        same &= set ? m : ~m;
+      }
+      if (ok) {
+        const int rank = __popcll(same & below);
+        const int pos = hist[wave * E + e] + rank;
+        p.perm[pos] = a;
+        if (p.inv) p.inv[a] = pos;
+        // the lowest lane of each group advances that expert's cursor; every lane of
+        // the wave has read the cursor above before this store executes
+        __builtin_amdgcn_wave_barrier();
+        if (rank == 0) hist[wave * E + e] += __popcll(same);
+      } else {
+        __builtin_amdgcn_wave_barrier();
+        if (in && p.inv) p.inv[a] = -1;
+      }
       __builtin_amdgcn_wave_barrier();
-      if (rank == 0) hist[wave * E + e] += __popcll(same);
-    } else {
-      __builtin_amdgcn_wave_barrier();
-      if (in && p.inv) p.inv[a] = -1;
     }
-    __builtin_amdgcn_wave_barrier();
   }
 }
 

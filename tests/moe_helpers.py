@@ -26,6 +26,20 @@ def oracle_weights(spec: synth.Spec, layer: dict | None = None) -> ExpertWeights
                          lambda e: synth.expert_down(spec, e))
 
 
+def prefetched_weights(spec: synth.Spec, experts, threads: int = 16) -> ExpertWeights:
+    """Oracle view of the given experts' weights, generated on the host in parallel."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    experts = sorted(set(int(e) for e in experts))
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        gu = dict(zip(experts, ex.map(lambda e: synth.expert_gate_up(spec, e), experts)))
+        dn = dict(zip(experts, ex.map(lambda e: synth.expert_down(spec, e), experts)))
+    if spec.weight == "fp8":
+        return ExpertWeights("fp8", lambda e: gu[e][0], lambda e: dn[e][0], spec.scale,
+                             lambda e: gu[e][1], lambda e: dn[e][1])
+    return ExpertWeights(spec.weight, lambda e: gu[e], lambda e: dn[e])
+
+
 def oracle_out(spec, x, idx, w, weights, tokens=None, mode="fast"):
     """Oracle result (rounded to the output type) as fp64, for all tokens or a subset."""
     _, out = forward(x, idx, w, weights, act=spec.act, E=spec.E, mode=mode, tokens=tokens)

@@ -12,7 +12,8 @@ import torch
 import mixture_experts_routed_topk_amd as m
 import synth
 from synth.device import device_layer
-from moe_helpers import assert_close, gpu_out_f64, oracle_out, oracle_weights, sample_tokens
+from moe_helpers import (assert_close, gpu_out_f64, oracle_out, oracle_weights, prefetched_weights,
+                         sample_tokens)
 
 pytestmark = pytest.mark.gpu
 
@@ -31,7 +32,8 @@ def _run(D, flags=0):
 def _full_check(spec, flags, tokens=None, what=""):
     D = device_layer(spec)
     out = gpu_out_f64(_run(D, flags))
-    W = oracle_weights(spec)
+    rows = np.arange(spec.T) if tokens is None else tokens
+    W = prefetched_weights(spec, np.unique(D["idx_host"][rows]))
     ref = oracle_out(spec, D["x_host"], D["idx_host"], D["w_host"], W, tokens=tokens)
     got = out if tokens is None else out[tokens]
     print(f"{what or spec.name} flags={flags}: T={spec.T} active={len(D['active'])}")
@@ -117,3 +119,92 @@ def test_bad_index_flag():
     idx[7, 1] = 0
     ref = oracle_out(spec, D["x_host"], idx, w, oracle_weights(spec))
     assert_close(out, ref, "bf16", "out-of-range slot ignored")
+
+
+# ----------------------------------------------------------------------------- decode path
+
+@pytest.mark.parametrize("flags", [0, m.FLAG_FORCE_DECODE, m.FLAG_FORCE_DECODE | m.FLAG_DETERMINISTIC])
+def test_qwen_decode_path(flags):
+    spec = synth.spec_for("qwen_decode_bf16")
+    D = device_layer(spec)
+    prob = m.problem_for(D["x"], D["idx"], D["w_gate_up"], D["w_down"], flags=flags)
+    assert "path=decode" in m.plan_describe(prob)
+    _full_check(spec, flags, what=f"qwen_decode decode-path flags={flags}")
+
+
+@pytest.mark.parametrize("shape", [
+    dict(T=64, H=256, I=256, E=4, k=2),       # > 16 tokens per expert: several token passes
+    dict(T=1, H=128, I=128, E=8, k=8),        # k == E, one token
+    dict(T=33, H=2304, I=128, E=16, k=3),     # H above one staged K slice (2048)
+    dict(T=5, H=384, I=2176, E=3, k=1),       # I above one staged K slice for the down projection
+])
+def test_decode_shapes(shape):
+    spec = synth.Spec("decode_bf16", act="bf16", weight="bf16", renorm=True, seed=11, **shape)
+    _full_check(spec, m.FLAG_FORCE_DECODE)
+
+
+def test_decode_matches_grouped_on_tiny_prefill():
+    # both paths on the same 96-token layer
+    spec = synth.Spec("both", T=96, H=256, I=128, E=6, k=2, act="bf16", weight="bf16", seed=12)
+    _full_check(spec, m.FLAG_FORCE_DECODE)
+    _full_check(spec, m.FLAG_FORCE_GROUPED)
+
+
+# ----------------------------------------------------------------------------- fp8 experts
+
+@pytest.mark.parametrize("scale", ["f32", "ue8m0"])
+@pytest.mark.parametrize("shape", [
+    dict(T=300, H=256, I=256, E=7, k=3),
+    dict(T=1, H=128, I=128, E=4, k=2),
+    dict(T=200, H=384, I=128, E=64, k=2),     # many empty experts
+    dict(T=40, H=128, I=256, E=3, k=3),       # k == E
+])
+def test_small_fp8(scale, shape):
+    spec = synth.Spec("small_fp8", act="bf16", weight="fp8", scale=scale, renorm=True, seed=5, **shape)
+    _full_check(spec, 0)
+
+
+@pytest.mark.parametrize("scale", ["f32", "ue8m0"])
+def test_small_fp8_deterministic(scale):
+    spec = synth.Spec("small_fp8d", T=129, H=256, I=256, E=5, k=2, act="bf16", weight="fp8", scale=scale, seed=6)
+    _full_check(spec, m.FLAG_DETERMINISTIC)
+
+
+@pytest.mark.parametrize("name", ["dsv3_fp8_f32scale", "dsv3_fp8_ue8m0"])
+def test_dsv3_fp8_sampled(name):
+    spec = synth.spec_for(name)
+    _full_check(spec, 0, tokens=sample_tokens(spec.T, 24))
+
+
+def test_dsv3_bf16_sampled():
+    spec = synth.spec_for("dsv3_prefill_bf16")
+    _full_check(spec, 0, tokens=sample_tokens(spec.T, 24))
+
+
+def test_quantize_rows_bit_exact():
+    from oracle.moe import quant_rows
+    from oracle.numerics import bf16_bits_to_f64
+    rng = np.random.default_rng(0)
+    x = (rng.standard_normal((37, 384)) * rng.uniform(1e-3, 1e3, (37, 1))).astype(np.float32)
+    x[5, 128:256] = 0.0
+    x[6, :128] = -0.0
+    bits = torch.from_numpy(x).to(torch.bfloat16)
+    q, s = m.quantize_rows_fp8(bits.cuda())
+    torch.cuda.synchronize()
+    xr = bf16_bits_to_f64(bits.view(torch.int16).numpy().view(np.uint16)).astype(np.float32)
+    rq, rs = quant_rows(xr)
+    assert np.array_equal(q.cpu().numpy(), rq)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+
+
+def test_quantize_rows_config_hidden_bit_exact():
+    # the fp8 layer's own hidden states, all 4096 x 7168
+    from oracle.moe import quant_rows
+    from oracle.numerics import bf16_bits_to_f64
+    spec = synth.spec_for("dsv3_fp8_f32scale")
+    xh = synth.hidden(spec)
+    q, s = m.quantize_rows_fp8(torch.from_numpy(xh.view(np.int16)).view(torch.bfloat16).cuda())
+    torch.cuda.synchronize()
+    rq, rs = quant_rows(bf16_bits_to_f64(xh).astype(np.float32))
+    assert np.array_equal(q.cpu().numpy(), rq)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32))
