@@ -92,7 +92,8 @@ typedef struct {
 
 /* Shape rules checked by every call taking a moe_problem:
  *   H % 128 == 0, I % 64 == 0 (f32, bf16 weights); H % 128 == 0, I % 128 == 0 (fp8);
- *   1 <= E <= 1024, 1 <= k <= E, T * k < 2^31, H, I <= 65536.                      */
+ *   1 <= E <= 1024, 1 <= k <= E, T * k < 2^31, H, I <= 65536, and each of hidden,
+ *   the intermediate [T*k, I] rows and one expert's W_gate_up below 4 GiB.            */
 
 /* ABI version of the loaded library (MOE_ABI_VERSION). */
 int moe_abi_version(void);

@@ -48,6 +48,12 @@ moe_status validate_problem(const moe_problem* p) {
   const int64_t items_gu = max_mtiles(A, p->E, 64) * (2 * (int64_t)p->I / 64);
   const int64_t items_dn = max_mtiles(A, p->E, 64) * ((int64_t)p->H / 64);
   if (items_gu >= (int64_t(1) << 31) || items_dn >= (int64_t(1) << 31)) return MOE_ERR_BAD_SHAPE;
+  // the grouped kernels address rows with 32-bit byte offsets: hidden [T,H], the SwiGLU
+  // rows [T*k, I] and one expert's weight matrix must each stay below 4 GiB
+  const int64_t esz = p->weight_dtype == MOE_F32 ? 4 : 2;
+  const int64_t lim = int64_t(1) << 32;
+  if (p->T * p->H * esz >= lim || A * p->I * esz >= lim || 2 * (int64_t)p->I * p->H * esz >= lim)
+    return MOE_ERR_BAD_SHAPE;
   return MOE_OK;
 }
 
@@ -204,7 +210,8 @@ moe_status moe_plan_describe(const moe_problem* p, char* buf, size_t len) {
   const char* sname = p->scale_fmt == MOE_SCALE_F32 ? "f32" : (p->scale_fmt == MOE_SCALE_UE8M0 ? "ue8m0" : "none");
   const char* kern = pl.path == kDecode ? "stream_weights_16tok_mfma16x16x32"
                      : p->weight_dtype == MOE_F32 ? "fma_64x64"
-                     : p->weight_dtype == MOE_BF16 ? "mfma16x16x32_bf16_128x128" : "mfma16x16x128_e4m3_128x128";
+                     : p->weight_dtype == MOE_BF16 ? "mfma32x32x16_bf16_128x256"
+                                                   : "gateup_mfma32x32x16_on_widened_e4m3_128x128+down_mfma16x16x128_e4m3_128x256";
   snprintf(buf, len, "path=%s weights=%s scales=%s kernels=%s combine=%s workspace_bytes=%zu",
            pl.path == kDecode ? "decode" : "grouped", wname, sname, kern,
            (p->flags & MOE_FLAG_DETERMINISTIC) ? "slot_rows" : "atomic_f32", L.total);
@@ -373,10 +380,10 @@ moe_status moe_experts_forward(const moe_problem* p, const void* hidden, const i
     MOE_HIP_CHECK(launch_down_f32(dn, max_mtiles(A, p->E, pl.bm) * dn.NT, s));
     MOE_HIP_CHECK(stage_mark(MOE_STAGE_DOWN, 1, s));
   } else {
-    gu.NT = p->I / 64;
-    dn.NT = p->H / 128;
+    gu.NT = (p->I + gateup_mfma_cols(fp8) - 1) / gateup_mfma_cols(fp8);
+    dn.NT = (p->H + down_mfma_cols(fp8) - 1) / down_mfma_cols(fp8);
     MOE_HIP_CHECK(stage_mark(MOE_STAGE_GATE_UP, 0, s));
-    MOE_HIP_CHECK(launch_gateup_mfma(gu, fp8, persistent_grid(dev->cus, 2, max_mtiles(A, p->E, pl.bm) * gu.NT), s));
+    MOE_HIP_CHECK(launch_gateup_mfma(gu, fp8, persistent_grid(dev->cus, 1, max_mtiles(A, p->E, pl.bm) * gu.NT), s));
     MOE_HIP_CHECK(stage_mark(MOE_STAGE_GATE_UP, 1, s));
     if (fp8) {
       MOE_HIP_CHECK(stage_mark(MOE_STAGE_QUANT_ACT, 0, s));
@@ -386,7 +393,7 @@ moe_status moe_experts_forward(const moe_problem* p, const void* hidden, const i
       MOE_HIP_CHECK(stage_mark(MOE_STAGE_QUANT_ACT, 1, s));
     }
     MOE_HIP_CHECK(stage_mark(MOE_STAGE_DOWN, 0, s));
-    MOE_HIP_CHECK(launch_down_mfma(dn, fp8, persistent_grid(dev->cus, 2, max_mtiles(A, p->E, pl.bm) * dn.NT), s));
+    MOE_HIP_CHECK(launch_down_mfma(dn, fp8, persistent_grid(dev->cus, 1, max_mtiles(A, p->E, pl.bm) * dn.NT), s));
     MOE_HIP_CHECK(stage_mark(MOE_STAGE_DOWN, 1, s));
   }
 

@@ -63,6 +63,13 @@ __device__ __forceinline__ f32x4 mfma_16x16x32_bf16(bf16x8 a, bf16x8 b, f32x4 c)
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// C[32x32] += A[32x16] * B[16x32]; lane l holds A row (l & 31) and B column (l & 31),
+// eight consecutive k of group (l >> 5); C element r of lane l sits at column (l & 31),
+// row 8*(r/4) + 4*(l >> 5) + (r % 4).
+__device__ __forceinline__ f32x16 mfma_32x32x16_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
 // C[16x16] += A[16x128] * B[128x16] with e4m3 operands (32 bytes per lane), unit
 // block scales (E8M0 exponent 127 = 2^0 on both sides).
 __device__ __forceinline__ f32x4 mfma_16x16x128_e4m3(i32x8 a, i32x8 b, f32x4 c) {

@@ -5,53 +5,75 @@
 // MLP of the "deepgemm_megamoe" row and the "SonicMoE" section (up projection,
 // SwiGLU, down projection).  Two kernels share one main loop:
 //
-//   gate_up : rows = hidden rows gathered through the sorted permutation,
-//             B = W_gate_up[e] ([2I, H], K = H contiguous).  A 128-row B tile holds
-//             64 gate rows and the 64 matching up rows, so the SwiGLU
-//             a = silu(gate) * up is formed in registers (stored as bf16, or as
-//             float32 for the fp8 path, which quantises it per 128 columns next).
-//   down    : rows = the SwiGLU rows (already in sorted order), B = W_down[e]
+//   gate_up : rows = hidden rows gathered through the sorted permutation, weights
+//             W_gate_up[e] ([2I, H], K = H contiguous).  The weight tile holds gate
+//             rows and the matching up rows, and every wave owns both halves of its
+//             columns, so a = silu(gate) * up is formed in registers (stored as bf16,
+//             or as float32 for the fp8 path, which quantises it per 128 columns next).
+//   down    : rows = the SwiGLU rows (already in sorted order), weights W_down[e]
 //             ([H, I], K = I contiguous).  The epilogue scales each row by its
 //             routing weight and adds it into the token's float32 output row
 //             (hardware float atomics), or stores it to the slot's own row for the
 //             deterministic combine.
 //
-// Operand kinds:
-//   kOpBf16    bf16 operands, v_mfma_f32_16x16x32_bf16.
-//   kOpFp8     OCP e4m3 operands with 128x128 block scales ("FP8 and FP4 quantized
-//              experts" section and note of the same page: float32 or UE8M0 block
-//              scales used directly, dynamic per-row activation scales), on
-//              v_mfma_scale_f32_16x16x128_f8f6f4.  One K tile is one 128-wide scale
-//              block, so each MFMA yields that block's partial product, added to the
-//              float32 accumulator times (activation row scale) * (weight block scale).
-//   kOpFp8Wide The same e4m3 operands widened exactly to bf16 on their way into LDS
-//              (v_cvt_scalef32_pk_bf16_fp8 with scale 1) and multiplied on the bf16
-//              MFMA.  gfx950's fp8 MFMAs sum their products with a precision of about
-//              2^-13 of the sum of magnitudes (measured), while the bf16 MFMA sums
-//              exact products in float32.  The gate/up projection feeds the e4m3
-//              quantisation of the SwiGLU output, whose codes flip on such errors, so
-//              it uses this kind; the down projection feeds nothing but the output
-//              and uses kOpFp8.
+// Tiling (one 512-thread block per CU, two waves per SIMD, so one wave's LDS and memory
+// waits are covered by the other's MFMAs): a 256-row x BN-column tile, 8 waves in a
+// 2 x 4 grid, each wave 128 rows x BN/4 columns.  Both operands are staged through LDS
+// in 128-byte rows (one K tile) whose 16-byte chunks are XOR-swizzled by (row & 7), so
+// fragment reads of 8 consecutive rows hit distinct banks; two LDS buffers, the global
+// loads of tile kt+1 in flight (in registers) while tile kt is multiplied.  Per CU this
+// moves (256 + BN) * 2 bytes of operands per K element for 2 * 256 * BN flops.  An
+// expert's rows are split evenly over its M tiles (multiples of 32 rows, at most 256),
+// and row fragments past the end of a tile are skipped.  The grid is persistent; work
+// items are (expert, N tile, M tile) with M fastest, and each round hands every XCD
+// (blockIdx % 8) a contiguous run of items, so the M tiles sharing a weight tile run at
+// the same pace on one XCD and meet in its L2.
 //
-// Tiles: 128 rows x 128 columns x 128 bytes of K in LDS, 256 threads = 4 waves in a
-// 2 x 2 grid, 64 x 64 per wave (4 x 4 MFMA fragments).  Operands are staged through
-// LDS, double buffered, in rows of 128 bytes whose 16-byte chunks are XOR-swizzled by
-// (row & 7) so the fragment reads of 8 consecutive rows hit distinct banks.  The grid
-// is persistent; work items are (expert, N tile, M tile) with M fastest, and each
-// round hands every XCD (blockIdx % 8) a contiguous run of items, so the M tiles that
-// share one weight tile run together on one XCD and meet in its L2.
+// Operand kinds (measured on MI355X: v_mfma_f32_32x32x16_bf16 sustains 88% of the
+// bf16 peak where the 16x16x32 form sustains half of it; v_mfma_scale 16x16x128 fp8
+// sustains 88% of the fp8 peak):
+//   kOpBf16    bf16, 32x32x16 MFMA, BN = 256 (wave 128 x 64: 4 x 2 fragments).
+//   kOpFp8     OCP e4m3 with 128x128 block scales ("FP8 and FP4 quantized experts"
+//              section and note of the same page: float32 or UE8M0 block scales used
+//              directly, dynamic per-row activation scales), 16x16x128 fp8 MFMA,
+//              BN = 256 (wave 128 x 64: 8 x 4 fragments).  One MFMA spans one
+//              128-wide scale block, so its result is added to the float32
+//              accumulator times (activation row scale) * (weight block scale).
+//   kOpFp8Wide The same e4m3 operands widened exactly to bf16 while being written to
+//              LDS (v_cvt_scalef32_pk_bf16_fp8, scale 1) and multiplied on the bf16
+//              MFMA, the two scales applied at the end of each 128-wide block;
+//              BN = 128 (wave 128 x 32: 16 gate + 16 up columns in one fragment,
+//              paired across lanes), since the per-block partial sums need a second
+//              set of accumulators.  gfx950's fp8 MFMAs sum their products
+//              with a precision of about 2^-13 of the sum of magnitudes (measured);
+//              the gate/up projection feeds the e4m3 quantisation of the SwiGLU
+//              output, whose codes flip on such errors, so it uses this kind; the down
+//              projection uses kOpFp8.
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
 namespace moe {
 namespace {
 
-constexpr int BM = 128, BN = 128, ROWB = 128;  // tile rows, tile columns, LDS bytes of K per row
-constexpr int kThreads = 256;
-constexpr int kTileBytes = 128 * ROWB;         // 16 KB per operand tile
+constexpr int kThreads = 512;          // 8 waves: 2 (rows) x 4 (columns)
+constexpr int BM = 256;
+constexpr int ROWB = 128;               // LDS bytes per tile row (one K tile)
 
 enum { kGateUp = 0, kDownAtomic = 1, kDownSlots = 2 };
 enum { kOpBf16 = 0, kOpFp8 = 1, kOpFp8Wide = 2 };
+
+template <int OP> struct Cfg;
+template <> struct Cfg<kOpBf16> {       // 32x32x16 bf16, wave 128 x 64
+  static constexpr int FR = 32, MFRAG = 4, NFRAG = 2, BN = 256, KTILE = 64, GB = 128;
+};
+template <> struct Cfg<kOpFp8> {        // 16x16x128 e4m3, wave 128 x 64
+  static constexpr int FR = 16, MFRAG = 8, NFRAG = 4, BN = 256, KTILE = 128, GB = 128;
+};
+template <> struct Cfg<kOpFp8Wide> {    // 32x32x16 bf16 on widened e4m3, wave 128 x 32 (16 gate + 16 up)
+  static constexpr int FR = 32, MFRAG = 4, NFRAG = 1, BN = 128, KTILE = 64, GB = 64;
+};
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * ROWB + ((chunk ^ (row & 7)) << 4); }
 
@@ -74,32 +96,64 @@ __device__ __forceinline__ void widen_e4m3x16(const i32x4 raw, i32x4& lo, i32x4&
 }
 
 template <int MODE, int OP>
-__global__ __launch_bounds__(kThreads, 2) void grouped_mfma_kernel(GroupedArgs g) {
+__global__ __launch_bounds__(kThreads, 1) void grouped_mfma_kernel(GroupedArgs g) {
+  using C = Cfg<OP>;
+  constexpr bool F8 = OP == kOpFp8;
+  constexpr bool WIDE = OP == kOpFp8Wide;
   constexpr bool SCALED = OP != kOpBf16;
-  constexpr int ESZ = OP == kOpBf16 ? 2 : 1;          // bytes per element in global memory
-  constexpr int KTILE = OP == kOpFp8 ? 128 : 64;      // K elements per LDS tile
-  constexpr int TPB = 128 / KTILE;                    // K tiles per 128-wide scale block
-  constexpr int GROWB = KTILE * ESZ;                  // global bytes per row per K tile
-  constexpr int CPR = GROWB / 16;                     // 16-byte global chunks per row (8 or 4)
-  constexpr int RPP = kThreads / CPR;                 // rows covered per loader pass (32 or 64)
-  constexpr int NLD = 128 / RPP;                      // loader passes per operand (4 or 2)
+  constexpr int BN = C::BN;
+  constexpr int WM = 128, WN = BN / 4;               // wave tile
+  constexpr int TPB = 128 / C::KTILE;                // K tiles per 128-wide scale block
+  constexpr int CPR = C::GB / 16;                    // 16-byte global chunks per row per tile
+  constexpr int RPP = kThreads / CPR;                // rows per loader pass
+  constexpr int ANL = BM / RPP;                      // row loads per thread
+  constexpr int BNL = BN / RPP;                      // weight loads per thread
+  constexpr int ESZ = OP == kOpBf16 ? 2 : 1;         // bytes per element in memory
+  constexpr int MG = F8 ? 2 : 1;                     // row fragments per 32 rows
+  using AccT = typename std::conditional<F8, f32x4, f32x16>::type;
 
-  __shared__ __attribute__((aligned(16))) char sA[2][kTileBytes];
-  __shared__ __attribute__((aligned(16))) char sB[2][kTileBytes];
-  __shared__ __attribute__((aligned(16))) float sSa[2][BM];  // activation row scales of the tile's block
-  __shared__ float sSb[2][2];                                // weight block scales (tile rows <64, >=64)
+  __shared__ __attribute__((aligned(16))) char sA[2][BM * ROWB];
+  __shared__ __attribute__((aligned(16))) char sB[2][BN * ROWB];
+  __shared__ __attribute__((aligned(16))) float sSa[2][BM];  // activation row scales of the stage's block
+  __shared__ float sSb[2][2];                                // weight block scales: gate/first half, up/second half
+  __shared__ int sTok[BM];                                   // epilogue: token (atomic) or slot (rows)
+  __shared__ float sWt[BM];                                  // epilogue: routing weight
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const int gx = gridDim.x >> 3;
   const int xcd = blockIdx.x & 7, xslot = blockIdx.x >> 3;
   const int n_items = g.mt[g.E] * g.NT;
-  const int KT = g.K / KTILE;
-  const int KB = g.K / 128;                           // scale blocks along K
-  const char* __restrict__ A = static_cast<const char*>(g.a);
-  const char* __restrict__ B = static_cast<const char*>(g.b);
+  const int KT = g.K / C::KTILE;
+  const int KB = g.K / 128;
+  const char* __restrict__ Abase = static_cast<const char*>(g.a);
+  const int lc = tid % CPR, lr = tid / CPR;          // loader: chunk lc of rows lr + RPP * i
+  const int ncols = MODE == kGateUp ? g.I : g.H;     // output columns of the whole GEMM
+  const int l7 = lane & 7;
 
-  const int lc = tid % CPR, lr = tid / CPR;           // loader: chunk lc of rows lr + RPP * i
+  // column offset (in tile rows) of this wave's fragment j inside the weight tile
+  // (gate/up, bf16: fragment 0 holds gate rows, fragment 1 the matching up rows;
+  //  fp8 widened: the wave's single fragment holds 16 gate rows then the 16 up rows)
+  auto b_frag_row = [&](int j) __attribute__((always_inline)) -> int {
+    if (MODE == kGateUp && !WIDE) return (j == 0 ? 0 : BN / 2) + wn * (WN / 2);
+    return wn * WN + j * C::FR;
+  };
+
+  // LDS byte offsets of this lane's fragment reads (swizzle term depends only on lane & 7,
+  // since every fragment starts on a multiple of 8 rows)
+  uint32_t a_lds[4], b_lds[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    if constexpr (F8) {                              // s = 0, 1: the two 16-byte halves of 32 bytes
+      const int ch = 2 * (lane >> 4) + (s & 1);
+      a_lds[s] = (wm * WM + (lane & 15)) * ROWB + ((ch ^ l7) << 4);
+      b_lds[s] = (lane & 15) * ROWB + ((ch ^ l7) << 4);
+    } else {
+      const int ch = 2 * s + (lane >> 5);
+      a_lds[s] = (wm * WM + (lane & 31)) * ROWB + ((ch ^ l7) << 4);
+      b_lds[s] = (lane & 31) * ROWB + ((ch ^ l7) << 4);
+    }
+  }
 
   for (int base = 0; base < n_items; base += gridDim.x) {
     const int w = base + xcd * gx + xslot;
@@ -109,231 +163,274 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_mfma_kernel(GroupedArgs g
     const int local = w - g.mt[e] * g.NT;
     const int nt = local / mt_e;
     const int mloc = local - nt * mt_e;
-    const int row0 = g.offsets[e] + mloc * BM;
-    const int rows = min(BM, g.offsets[e + 1] - row0);
+    // the expert's rows split evenly over its M tiles (multiples of 32 rows), so tiles that
+    // share a weight tile advance at the same pace and meet in L2
+    const int cnt = g.offsets[e + 1] - g.offsets[e];
+    const int per = min(BM, ((cnt + mt_e - 1) / mt_e + 31) & ~31);
+    const int row0 = g.offsets[e] + mloc * per;
+    const int rows = min(per, g.offsets[e + 1] - row0);
+    if (rows <= 0) continue;
+    const char* __restrict__ Bexp = static_cast<const char*>(g.b) + (int64_t)e * g.b_expert_stride * ESZ;
 
-    auto b_row = [&](int r) -> int {   // global weight row of tile row r
-      if (MODE == kGateUp) return (r < 64) ? nt * 64 + r : g.I + nt * 64 + (r - 64);
-      return nt * BN + r;
-    };
-    auto a_src = [&](int r) -> int64_t {  // source row of tile row r (rows past the end repeat the last)
-      const int p = row0 + min(r, rows - 1);
-      return g.a_rows ? (int64_t)(g.a_rows[p] / g.a_row_div) : (int64_t)p;
-    };
-
-    const char* pa[NLD];
-    const char* pb[NLD];
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int r = lr + RPP * i;
-      pa[i] = A + a_src(r) * g.lda * ESZ + lc * 16;
-      pb[i] = B + ((int64_t)e * g.b_expert_stride + (int64_t)b_row(r) * g.K) * ESZ + lc * 16;
-    }
-    // scale sources: threads 0..127 own one activation row, 128..129 one weight block
-    const float* psa = nullptr;
-    const void* psb = nullptr;
-    if (SCALED) {
-      if (tid < BM) psa = g.a_scale + a_src(tid) * KB;
-      else if (tid < BM + 2) {
-        const int64_t blk = (int64_t)e * (g.b_rows / 128) + b_row((tid - BM) * 64) / 128;
-        psb = g.b_scale_ue8m0 ? (const void*)(static_cast<const uint8_t*>(g.b_scale) + blk * KB)
-                              : (const void*)(static_cast<const float*>(g.b_scale) + blk * KB);
+    // global weight row of tile row r; rows past the matrix repeat its last valid row
+    auto b_row = [&](int r) __attribute__((always_inline)) -> int {
+      if (MODE == kGateUp) {
+        if (WIDE) {   // 32-row groups: 16 gate rows, then the matching 16 up rows
+          const int c = min(nt * (BN / 2) + (r / 32) * 16 + (r % 16), g.I - 1);
+          return (r % 32) < 16 ? c : g.I + c;
+        }
+        const int c = min(nt * (BN / 2) + (r % (BN / 2)), g.I - 1);
+        return r < BN / 2 ? c : g.I + c;
       }
-    }
-    auto load_scale = [&](int kt) -> float {
-      if (!SCALED) return 0.f;
-      const int kb = kt / TPB;
-      if (psa) return psa[kb];
-      if (psb) return g.b_scale_ue8m0 ? ue8m0_to_f32(static_cast<const uint8_t*>(psb)[kb])
-                                      : static_cast<const float*>(psb)[kb];
-      return 0.f;
+      return min(nt * BN + r, g.H - 1);
     };
-    auto store_scale = [&](int buf, float v) {
-      if (!SCALED) return;
-      if (tid < BM) sSa[buf][tid] = v;
-      else if (tid < BM + 2) sSb[buf][tid - BM] = v;
+    auto a_src = [&](int r) __attribute__((always_inline)) -> int {   // source row of tile row r
+      const int p = row0 + min(r, rows - 1);                          // (rows past the end repeat the last)
+      return g.a_rows ? g.a_rows[p] / g.a_row_div : p;
     };
-    auto store_tiles = [&](int buf, const i32x4* ra, const i32x4* rb) {
+    // 32-bit byte offsets of this thread's loader rows (operands are < 4 GiB, checked on the host)
+    uint32_t aoff[ANL], boff[BNL];
 #pragma unroll
-      for (int i = 0; i < NLD; ++i) {
+    for (int i = 0; i < ANL; ++i) aoff[i] = (uint32_t)a_src(lr + RPP * i) * (uint32_t)(g.lda * ESZ) + lc * 16;
+#pragma unroll
+    for (int i = 0; i < BNL; ++i) boff[i] = (uint32_t)b_row(lr + RPP * i) * (uint32_t)(g.K * ESZ) + lc * 16;
+    // scales: thread t owns activation row t; threads 0..1 also one weight block each
+    const float* psa = (SCALED && tid < BM) ? g.a_scale + (int64_t)a_src(tid) * KB : nullptr;
+    const char* psb = nullptr;
+    if (SCALED && tid < 2) {
+      // block of the first gate/down row (thread 0) and of the first up / second-half row (thread 1)
+      const int64_t blk = (int64_t)e * (g.b_rows / 128) + b_row(tid == 0 ? 0 : (WIDE ? 16 : BN / 2)) / 128;
+      psb = static_cast<const char*>(g.b_scale) + blk * KB * (g.b_scale_ue8m0 ? 1 : 4);
+    }
+    if (tid < rows) {
+      const int slot = g.perm[row0 + tid];
+      sTok[tid] = MODE == kDownAtomic ? slot / g.k : slot;
+      sWt[tid] = g.topk_w[slot];
+    }
+
+    AccT acc[C::MFRAG][C::NFRAG], part[WIDE ? C::MFRAG : 1][WIDE ? C::NFRAG : 1];
+#pragma unroll
+    for (int i = 0; i < C::MFRAG; ++i)
+#pragma unroll
+      for (int j = 0; j < C::NFRAG; ++j) acc[i][j] = AccT{};
+#pragma unroll
+    for (int i = 0; i < (WIDE ? C::MFRAG : 1); ++i)
+#pragma unroll
+      for (int j = 0; j < (WIDE ? C::NFRAG : 1); ++j) part[i][j] = AccT{};
+
+    i32x4 ra[ANL], rb[BNL];
+    float rsa = 0.f, rsb = 0.f;
+
+    auto load = [&](int kt) __attribute__((always_inline)) {   // global loads of tile kt into registers
+      const uint32_t ko = (uint32_t)kt * C::GB;
+#pragma unroll
+      for (int i = 0; i < ANL; ++i) ra[i] = *reinterpret_cast<const i32x4*>(Abase + (aoff[i] + ko));
+#pragma unroll
+      for (int i = 0; i < BNL; ++i) rb[i] = *reinterpret_cast<const i32x4*>(Bexp + (boff[i] + ko));
+      if (SCALED) {
+        if (psa) rsa = psa[kt / TPB];
+        if (psb) rsb = g.b_scale_ue8m0 ? ue8m0_to_f32(reinterpret_cast<const uint8_t*>(psb)[kt / TPB])
+                                      : reinterpret_cast<const float*>(psb)[kt / TPB];
+      }
+    };
+    auto store = [&](int buf) __attribute__((always_inline)) {  // registers -> LDS buffer buf
+#pragma unroll
+      for (int i = 0; i < ANL; ++i) {
         const int r = lr + RPP * i;
-        if (OP == kOpFp8Wide) {
+        if constexpr (WIDE) {
           i32x4 lo, hi;
           widen_e4m3x16(ra[i], lo, hi);
           *reinterpret_cast<i32x4*>(&sA[buf][swz(r, 2 * lc)]) = lo;
           *reinterpret_cast<i32x4*>(&sA[buf][swz(r, 2 * lc + 1)]) = hi;
+        } else {
+          *reinterpret_cast<i32x4*>(&sA[buf][swz(r, lc)]) = ra[i];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < BNL; ++i) {
+        const int r = lr + RPP * i;
+        if constexpr (WIDE) {
+          i32x4 lo, hi;
           widen_e4m3x16(rb[i], lo, hi);
           *reinterpret_cast<i32x4*>(&sB[buf][swz(r, 2 * lc)]) = lo;
           *reinterpret_cast<i32x4*>(&sB[buf][swz(r, 2 * lc + 1)]) = hi;
         } else {
-          *reinterpret_cast<i32x4*>(&sA[buf][swz(r, lc)]) = ra[i];
           *reinterpret_cast<i32x4*>(&sB[buf][swz(r, lc)]) = rb[i];
+        }
+      }
+      if (SCALED) {
+        if (tid < BM) sSa[buf][tid] = rsa;
+        if (tid < 2) sSb[buf][tid] = rsb;
+      }
+    };
+
+    // multiply the tile in LDS buffer cur; NI = active row fragments of this wave
+    auto compute = [&](auto NI_, int kt) __attribute__((always_inline)) {
+      constexpr int NI = decltype(NI_)::value;
+      const int cur = kt & 1;
+      const char* As = sA[cur];
+      const char* Bs = sB[cur];
+      if constexpr (!F8) {
+        // 32x32x16: lane holds row (lane & 31), K chunk 2s + (lane >> 5) of the tile
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          bf16x8 bfr[C::NFRAG];
+#pragma unroll
+          for (int j = 0; j < C::NFRAG; ++j)
+            bfr[j] = *reinterpret_cast<const bf16x8*>(Bs + b_lds[s] + b_frag_row(j) * ROWB);
+#pragma unroll
+          for (int i = 0; i < NI; ++i) {
+            const bf16x8 afr = *reinterpret_cast<const bf16x8*>(As + a_lds[s] + i * C::FR * ROWB);
+#pragma unroll
+            for (int j = 0; j < C::NFRAG; ++j) {
+              if constexpr (WIDE) part[i][j] = mfma_32x32x16_bf16(afr, bfr[j], part[i][j]);
+              else acc[i][j] = mfma_32x32x16_bf16(afr, bfr[j], acc[i][j]);
+            }
+          }
+        }
+        if constexpr (WIDE) {
+          if ((kt + 1) % TPB == 0) {
+            // end of a 128-wide scale block: acc += part * (row scale) * (column block scale)
+#pragma unroll
+            for (int j = 0; j < C::NFRAG; ++j) {
+              const float sb = sSb[cur][(lane & 16) ? 1 : 0];   // columns 0..15 gate, 16..31 up
+#pragma unroll
+              for (int i = 0; i < NI; ++i) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                  const f32x4 sa =
+                      *reinterpret_cast<const f32x4*>(&sSa[cur][wm * WM + i * 32 + 8 * q + 4 * (lane >> 5)]);
+#pragma unroll
+                  for (int u = 0; u < 4; ++u)
+                    acc[i][j][4 * q + u] = fmaf(part[i][j][4 * q + u], sa[u] * sb, acc[i][j][4 * q + u]);
+                }
+                part[i][j] = AccT{};
+              }
+            }
+          }
+        }
+      } else {
+        // 16x16x128 fp8: lane holds row (lane & 15), K bytes 32 * (lane >> 4) .. +32 of the tile
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int jh = 0; jh < 2; ++jh) {                 // column fragments in two halves
+          i32x8 bfr[C::NFRAG / 2];
+          float sb[C::NFRAG / 2];
+#pragma unroll
+          for (int jj = 0; jj < C::NFRAG / 2; ++jj) {
+            const int j = jh * (C::NFRAG / 2) + jj;
+            const i32x4 lo = *reinterpret_cast<const i32x4*>(Bs + b_lds[0] + b_frag_row(j) * ROWB);
+            const i32x4 hi = *reinterpret_cast<const i32x4*>(Bs + b_lds[1] + b_frag_row(j) * ROWB);
+            bfr[jj] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            sb[jj] = sSb[cur][b_frag_row(j) >= BN / 2 ? 1 : 0];
+          }
+#pragma unroll
+          for (int i = 0; i < NI; ++i) {
+            const i32x4 lo = *reinterpret_cast<const i32x4*>(As + a_lds[0] + i * C::FR * ROWB);
+            const i32x4 hi = *reinterpret_cast<const i32x4*>(As + a_lds[1] + i * C::FR * ROWB);
+            const i32x8 afr = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            const f32x4 sa = *reinterpret_cast<const f32x4*>(&sSa[cur][wm * WM + i * C::FR + 4 * (lane >> 4)]);
+#pragma unroll
+            for (int jj = 0; jj < C::NFRAG / 2; ++jj) {
+              const int j = jh * (C::NFRAG / 2) + jj;
+              const f32x4 pr = mfma_16x16x128_e4m3(afr, bfr[jj], zero);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) acc[i][j][q] = fmaf(pr[q], sa[q] * sb[jj], acc[i][j][q]);
+            }
+          }
         }
       }
     };
 
-    f32x4 acc[4][4], part[4][4];   // part: running sum of the current scale block (kOpFp8Wide)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        part[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-
-    i32x4 ra[NLD], rb[NLD];
-    float rs = 0.f;
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      ra[i] = *reinterpret_cast<const i32x4*>(pa[i]);
-      rb[i] = *reinterpret_cast<const i32x4*>(pb[i]);
-    }
-    rs = load_scale(0);
-    store_tiles(0, ra, rb);
-    store_scale(0, rs);
-    __syncthreads();
-
-    for (int kt = 0; kt < KT; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < KT) {
-#pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-          ra[i] = *reinterpret_cast<const i32x4*>(pa[i] + (kt + 1) * GROWB);
-          rb[i] = *reinterpret_cast<const i32x4*>(pb[i] + (kt + 1) * GROWB);
-        }
-        rs = load_scale(kt + 1);
-      }
-      // keep the next tile's global loads in flight across the MFMA block: without
-      // these fences the scheduler sinks the LDS stores (and the waits on the loads)
-      // above the MFMAs, serialising every K step on memory latency
-      __builtin_amdgcn_sched_barrier(0);
-      if (OP != kOpFp8) {
-        // bf16 MFMA over the two 32-wide K steps of this tile
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          bf16x8 fa[4], fb[4];
-          const int ch = s * 4 + (lane >> 4);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = wm * 64 + i * 16 + (lane & 15);
-            fa[i] = *reinterpret_cast<const bf16x8*>(&sA[cur][swz(r, ch)]);
-          }
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            int r;
-            if (MODE == kGateUp) r = (j < 2 ? wn * 32 + j * 16 : 64 + wn * 32 + (j - 2) * 16) + (lane & 15);
-            else r = wn * 64 + j * 16 + (lane & 15);
-            fb[j] = *reinterpret_cast<const bf16x8*>(&sB[cur][swz(r, ch)]);
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              if (OP == kOpBf16) acc[i][j] = mfma_16x16x32_bf16(fa[i], fb[j], acc[i][j]);
-              else part[i][j] = mfma_16x16x32_bf16(fa[i], fb[j], part[i][j]);
-            }
-        }
-      } else {
-        i32x8 fa[4], fb[4];
-        const int c0 = 2 * (lane >> 4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = wm * 64 + i * 16 + (lane & 15);
-          const i32x4 lo = *reinterpret_cast<const i32x4*>(&sA[cur][swz(r, c0)]);
-          const i32x4 hi = *reinterpret_cast<const i32x4*>(&sA[cur][swz(r, c0 + 1)]);
-          fa[i] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = wn * 64 + j * 16 + (lane & 15);
-          const i32x4 lo = *reinterpret_cast<const i32x4*>(&sB[cur][swz(r, c0)]);
-          const i32x4 hi = *reinterpret_cast<const i32x4*>(&sB[cur][swz(r, c0 + 1)]);
-          fb[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
-        // one MFMA covers the whole 128-wide scale block: scale its result right away
-        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-        float sb[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) sb[j] = sSb[cur][wn];   // down tiles: rows of one 128-row block
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const f32x4 sa = *reinterpret_cast<const f32x4*>(&sSa[cur][wm * 64 + i * 16 + 4 * (lane >> 4)]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const f32x4 pr = mfma_16x16x128_e4m3(fa[i], fb[j], zero);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) acc[i][j][q] = fmaf(pr[q], sa[q] * sb[j], acc[i][j][q]);
-          }
-        }
-      }
-      if (OP == kOpFp8Wide && ((kt + 1) % TPB == 0)) {
-        // end of a 128-wide scale block: acc += part * (row scale) * (block scale)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const f32x4 sa = *reinterpret_cast<const f32x4*>(&sSa[cur][wm * 64 + i * 16 + 4 * (lane >> 4)]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            int rb0;
-            if (MODE == kGateUp) rb0 = (j < 2 ? wn * 32 + j * 16 : 64 + wn * 32 + (j - 2) * 16);
-            else rb0 = wn * 64 + j * 16;
-            const float sb = sSb[cur][rb0 >= 64 ? 1 : 0];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) acc[i][j][q] = fmaf(part[i][j][q], sa[q] * sb, acc[i][j][q]);
-            part[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-          }
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      if (kt + 1 < KT) {
-        store_tiles(cur ^ 1, ra, rb);
-        store_scale(cur ^ 1, rs);
-      }
+    // the K loop for a wave with NI active row fragments (no per-fragment branches inside)
+    auto kloop = [&](auto NI_) __attribute__((always_inline)) {
+      load(0);
+      store(0);
       __syncthreads();
+      for (int kt = 0; kt < KT; ++kt) {
+        if (kt + 1 < KT) load(kt + 1);
+        // keep the loads in flight across the MFMAs: without these fences the scheduler
+        // sinks the waits on the loads above the MFMA block
+        __builtin_amdgcn_sched_barrier(0);
+        compute(NI_, kt);
+        __builtin_amdgcn_sched_barrier(0);
+        if (kt + 1 < KT) store((kt + 1) & 1);
+        __syncthreads();
+      }
+    };
+    // row fragments of this wave that hold rows of the tile, in groups of 32 rows
+    const int groups = min(4, max(0, (rows - wm * WM + 31) / 32));
+    switch (groups) {
+      case 4: kloop(std::integral_constant<int, 4 * MG>{}); break;
+      case 3: kloop(std::integral_constant<int, 3 * MG>{}); break;
+      case 2: kloop(std::integral_constant<int, 2 * MG>{}); break;
+      case 1: kloop(std::integral_constant<int, 1 * MG>{}); break;
+      default: kloop(std::integral_constant<int, 0>{}); break;
     }
 
-    // epilogue; fragment (i, j) element q sits at tile row wm*64 + i*16 + 4*(lane>>4) + q,
-    // tile column (lane & 15) of fragment j
-    const int col_in = lane & 15;
-    if (MODE == kGateUp) {
+    // epilogue
+    if constexpr (F8) {
+      // 16x16 fragment (i, j): element q at row i*16 + 4*(lane>>4) + q, column j*16 + (lane & 15)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < C::MFRAG; ++i) {
+        if (wm * WM + i * 16 >= rows) break;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int r = wm * 64 + i * 16 + 4 * (lane >> 4) + q;
+          const int r = wm * WM + i * 16 + 4 * (lane >> 4) + q;
           if (r < rows) {
-            const int64_t o = (int64_t)(row0 + r) * g.I + nt * 64 + wn * 32 + col_in;
+            const float wt = sWt[r];
+            const int64_t tok = sTok[r];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-              const float gt = acc[i][j][q], up = acc[i][j + 2][q];
-              if (SCALED) static_cast<float*>(g.act_out)[o + j * 16] = silu_exact(gt) * up;
-              else static_cast<uint16_t*>(g.act_out)[o + j * 16] = (uint16_t)f32_to_bf16_bits(silu_fast(gt) * up);
+            for (int j = 0; j < C::NFRAG; ++j) {
+              const int col = nt * BN + b_frag_row(j) + (lane & 15);
+              if (col < ncols) {
+                if (MODE == kDownAtomic) unsafeAtomicAdd(g.acc_out + tok * g.H + col, wt * acc[i][j][q]);
+                else g.slot_out[tok * g.H + col] = wt * acc[i][j][q];
+              }
             }
           }
         }
       }
     } else {
+      // 32x32 fragment (i, j): element v at row i*32 + 8*(v/4) + 4*(lane>>5) + (v%4), column lane & 31
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < C::MFRAG; ++i) {
+        if (wm * WM + i * 32 >= rows) break;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int r = wm * 64 + i * 16 + 4 * (lane >> 4) + q;
-          if (r < rows) {
-            const int slot = g.perm[row0 + r];
-            const float wt = g.topk_w[slot];
-            const int64_t colbase = (int64_t)nt * BN + wn * 64 + col_in;
-            if (MODE == kDownAtomic) {
-              float* orow = g.acc_out + (int64_t)(slot / g.k) * g.H + colbase;
-#pragma unroll
-              for (int j = 0; j < 4; ++j) unsafeAtomicAdd(orow + j * 16, wt * acc[i][j][q]);
+        for (int v = 0; v < 16; ++v) {
+          const int r = wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          float up_w = 0.f;
+          if constexpr (WIDE) up_w = __shfl_xor(acc[i][0][v], 16);  // lane n (< 16) pairs with lane n + 16
+          if (r >= rows) continue;
+          if constexpr (MODE == kGateUp) {
+            if constexpr (WIDE) {
+              const float gt = acc[i][0][v], up = up_w;
+              const int col = nt * (BN / 2) + wn * 16 + (lane & 15);
+              if (!(lane & 16) && col < ncols)
+                static_cast<float*>(g.act_out)[(int64_t)(row0 + r) * g.I + col] = silu_exact(gt) * up;
             } else {
-              float* orow = g.slot_out + (int64_t)slot * g.H + colbase;
+              const int col = nt * (BN / 2) + wn * (WN / 2) + (lane & 31);
+              if (col < ncols) {
+                const float a = silu_fast(acc[i][0][v]) * acc[i][1][v];
+                static_cast<uint16_t*>(g.act_out)[(int64_t)(row0 + r) * g.I + col] = (uint16_t)f32_to_bf16_bits(a);
+              }
+            }
+          } else {
+            const float wt = sWt[r];
+            const int64_t tok = sTok[r];
 #pragma unroll
-              for (int j = 0; j < 4; ++j) orow[j * 16] = wt * acc[i][j][q];
+            for (int j = 0; j < C::NFRAG; ++j) {
+              const int col = nt * BN + b_frag_row(j) + (lane & 31);
+              if (col < ncols) {
+                if (MODE == kDownAtomic) unsafeAtomicAdd(g.acc_out + tok * g.H + col, wt * acc[i][j][v]);
+                else g.slot_out[tok * g.H + col] = wt * acc[i][j][v];
+              }
             }
           }
         }
       }
     }
+    __syncthreads();  // sTok / sWt / LDS tiles are reused by the next item
   }
 }
 
@@ -346,6 +443,8 @@ hipError_t launch(const GroupedArgs& g, int grid, hipStream_t s) {
 }  // namespace
 
 int grouped_mfma_bm() { return BM; }
+int gateup_mfma_cols(bool fp8) { return fp8 ? Cfg<kOpFp8Wide>::BN / 2 : Cfg<kOpBf16>::BN / 2; }
+int down_mfma_cols(bool fp8) { return fp8 ? Cfg<kOpFp8>::BN : Cfg<kOpBf16>::BN; }
 
 hipError_t launch_gateup_mfma(const GroupedArgs& g, bool fp8, int grid, hipStream_t s) {
   return fp8 ? launch<kGateUp, kOpFp8Wide>(g, grid, s) : launch<kGateUp, kOpBf16>(g, grid, s);

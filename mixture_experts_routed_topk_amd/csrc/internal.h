@@ -64,6 +64,8 @@ inline int64_t max_mtiles(int64_t A, int E, int bm) { return A / bm + (A < E ? A
 
 // bf16 / fp8 MFMA grouped GEMMs (persistent grid)
 int grouped_mfma_bm();
+int gateup_mfma_cols(bool fp8);   // SwiGLU columns per N tile of the gate/up kernel
+int down_mfma_cols(bool fp8);     // hidden columns per N tile of the down kernel
 hipError_t launch_gateup_mfma(const GroupedArgs& g, bool fp8, int grid, hipStream_t s);
 hipError_t launch_down_mfma(const GroupedArgs& g, bool fp8, int grid, hipStream_t s);
 
