@@ -210,8 +210,8 @@ moe_status moe_plan_describe(const moe_problem* p, char* buf, size_t len) {
   const char* sname = p->scale_fmt == MOE_SCALE_F32 ? "f32" : (p->scale_fmt == MOE_SCALE_UE8M0 ? "ue8m0" : "none");
   const char* kern = pl.path == kDecode ? "stream_weights_16tok_mfma16x16x32"
                      : p->weight_dtype == MOE_F32 ? "fma_64x64"
-                     : p->weight_dtype == MOE_BF16 ? "mfma32x32x16_bf16_128x256"
-                                                   : "gateup_mfma32x32x16_on_widened_e4m3_128x128+down_mfma16x16x128_e4m3_128x256";
+                     : p->weight_dtype == MOE_BF16 ? "mfma32x32x16_bf16_256x256_dma_ring4"
+                                                   : "gateup_mfma32x32x16_on_widened_e4m3_256x128+down_mfma16x16x128_e4m3_256x256";
   snprintf(buf, len, "path=%s weights=%s scales=%s kernels=%s combine=%s workspace_bytes=%zu",
            pl.path == kDecode ? "decode" : "grouped", wname, sname, kern,
            (p->flags & MOE_FLAG_DETERMINISTIC) ? "slot_rows" : "atomic_f32", L.total);
@@ -380,10 +380,13 @@ moe_status moe_experts_forward(const moe_problem* p, const void* hidden, const i
     MOE_HIP_CHECK(launch_down_f32(dn, max_mtiles(A, p->E, pl.bm) * dn.NT, s));
     MOE_HIP_CHECK(stage_mark(MOE_STAGE_DOWN, 1, s));
   } else {
-    gu.NT = (p->I + gateup_mfma_cols(fp8) - 1) / gateup_mfma_cols(fp8);
-    dn.NT = (p->H + down_mfma_cols(fp8) - 1) / down_mfma_cols(fp8);
+    const int gu_cols = fp8 ? gateup_fp8_cols() : gateup_bf16_cols();
+    const int dn_cols = fp8 ? down_fp8_cols() : down_bf16_cols();
+    gu.NT = (p->I + gu_cols - 1) / gu_cols;
+    dn.NT = (p->H + dn_cols - 1) / dn_cols;
     MOE_HIP_CHECK(stage_mark(MOE_STAGE_GATE_UP, 0, s));
-    MOE_HIP_CHECK(launch_gateup_mfma(gu, fp8, persistent_grid(dev->cus, 1, max_mtiles(A, p->E, pl.bm) * gu.NT), s));
+    const int gu_grid = persistent_grid(dev->cus, 1, max_mtiles(A, p->E, pl.bm) * gu.NT);
+    MOE_HIP_CHECK(fp8 ? launch_gateup_fp8(gu, gu_grid, s) : launch_gateup_bf16(gu, gu_grid, s));
     MOE_HIP_CHECK(stage_mark(MOE_STAGE_GATE_UP, 1, s));
     if (fp8) {
       MOE_HIP_CHECK(stage_mark(MOE_STAGE_QUANT_ACT, 0, s));
@@ -393,7 +396,8 @@ moe_status moe_experts_forward(const moe_problem* p, const void* hidden, const i
       MOE_HIP_CHECK(stage_mark(MOE_STAGE_QUANT_ACT, 1, s));
     }
     MOE_HIP_CHECK(stage_mark(MOE_STAGE_DOWN, 0, s));
-    MOE_HIP_CHECK(launch_down_mfma(dn, fp8, persistent_grid(dev->cus, 1, max_mtiles(A, p->E, pl.bm) * dn.NT), s));
+    const int dn_grid = persistent_grid(dev->cus, 1, max_mtiles(A, p->E, pl.bm) * dn.NT);
+    MOE_HIP_CHECK(fp8 ? launch_down_fp8(dn, dn_grid, s) : launch_down_bf16(dn, dn_grid, s));
     MOE_HIP_CHECK(stage_mark(MOE_STAGE_DOWN, 1, s));
   }
 

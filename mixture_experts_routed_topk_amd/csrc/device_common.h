@@ -76,6 +76,37 @@ __device__ __forceinline__ f32x4 mfma_16x16x128_e4m3(i32x8 a, i32x8 b, f32x4 c) 
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
+// C[32x32] += A[32x64] * B[64x32] with e4m3 operands (32 bytes per lane: lane l holds
+// A row / B column (l & 31) and 32 k of group (l >> 5)), unit block scales.
+__device__ __forceinline__ f32x16 mfma_32x32x64_e4m3(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// ---------------------------------------------------------------------------- LDS DMA
+// Global -> LDS loads that bypass the registers.  One instruction per wave: lane L
+// reads `base + off` and its data lands at LDS byte address m0 + 16 L (dwordx4) or
+// m0 + 4 L (dword; ubyte zero-extended to a dword).  `base` and `m0` are wave-uniform.
+// The compiler does not count these loads: every reader of the data waits for them
+// with wait_vmcnt<N>() (at most N vector-memory operations of this wave outstanding,
+// which retire in issue order) followed by a workgroup barrier.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+__device__ __forceinline__ void dma_lds_x4(const void* base, uint32_t off, uint32_t m0) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(m0) : "memory");
+}
+__device__ __forceinline__ void dma_lds_x1(const void* base, uint32_t off, uint32_t m0) {
+  asm volatile("global_load_lds_dword %0, %1" ::"v"(off), "s"(base), "{m0}"(m0) : "memory");
+}
+__device__ __forceinline__ void dma_lds_u8(const void* base, uint32_t off, uint32_t m0) {
+  asm volatile("global_load_lds_ubyte %0, %1" ::"v"(off), "s"(base), "{m0}"(m0) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // ---------------------------------------------------------------------------- misc
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
