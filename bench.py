@@ -109,6 +109,57 @@ def layer_totals(spec, active_count):
     return flops, float(byts)
 
 
+KERNEL_SOURCES = {   # (path, weight dtype, stage) -> kernel source files, for the traffic record
+    ("grouped", "bf16"): ["grouped_mfma.hip"],
+    ("grouped", "fp8"): ["grouped_mfma_fp8.hip"],
+    ("grouped", "f32"): ["grouped_f32.hip"],
+    ("decode", "bf16"): ["decode.hip"],
+}
+
+
+def kernel_digest(path: str, weight: str) -> tuple[str, str]:
+    """(name, sha256) of the dominant kernel's sources (its file + the shared device headers)."""
+    import hashlib
+    files = KERNEL_SOURCES[(path, weight)]
+    csrc = os.path.join(ROOT, "mixture_experts_routed_topk_amd", "csrc")
+    h = hashlib.sha256()
+    for f in files + ["device_common.h", "internal.h"]:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return files[0].rsplit(".", 1)[0], h.hexdigest()
+
+
+def recorded_traffic(kernel: str, stage: str, config: str, digest: str):
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE summary of this kernel
+    and workload, or None when there is none or the kernel source changed since."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{stage}_{config}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("    ") and ":" in line:
+                k, v = line.strip().split(":", 1)
+                rec[k.strip()] = v.strip()
+    if rec.get("kernel_source_sha256") != digest or "traffic_bytes_per_launch" not in rec:
+        return None
+    return float(rec["traffic_bytes_per_launch"])
+
+
+def copy_calibration(nbytes: int = 256 << 20, reps: int = 3):
+    """A plain device copy of a known size, run under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
+    to scale those counters to bytes: each of the `reps` launches reads and writes nbytes."""
+    import torch
+    x = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read_per_launch": nbytes, "bytes_written_per_launch": nbytes,
+                                           "launches": reps}}), flush=True)
+
+
 def cpu_baseline(spec, D, seconds: float):
     """The fp64 oracle (per-token loop over the k chosen experts) on a token sample."""
     import numpy as np
@@ -160,12 +211,18 @@ def main():
     ap.add_argument("--flags", type=int, default=0, help="MOE_FLAG_* bits passed to the forward")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 256 MiB device copy (counter calibration for the traffic figure)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this experts forward is a single-GPU library "
               "(no sharding, no collectives); run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import torch
     import mixture_experts_routed_topk_amd as m
@@ -243,8 +300,9 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": byts / (kavg * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
-    roof.update({"kernel": dominant, "avg_ms": kavg, "launches": len(kern_ms),
+    kname, digest = kernel_digest(plan.split()[0].split("=")[1], spec.weight)
+    roof["traffic"] = recorded_traffic(kname, dominant, args.config, digest)
+    roof.update({"kernel": f"{kname}:{dominant}", "kernel_source_sha256": digest, "avg_ms": kavg, "launches": len(kern_ms),
                  "algorithmic_flops": flops, "algorithmic_bytes": byts,
                  "mfma_frac": flops / (kavg * 1e-3) / 1e12 / peak_f,
                  "hbm_frac": byts / (kavg * 1e-3) / 1e9 / PEAK_HBM_GBS})
