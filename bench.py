@@ -110,7 +110,7 @@ def layer_totals(spec, active_count):
 
 
 KERNEL_SOURCES = {   # (path, weight dtype, stage) -> kernel source files, for the traffic record
-    ("grouped", "bf16"): ["grouped_mfma.hip"],
+    ("grouped", "bf16"): ["grouped_bf16.hip"],
     ("grouped", "fp8"): ["grouped_mfma_fp8.hip"],
     ("grouped", "f32"): ["grouped_f32.hip"],
     ("decode", "bf16"): ["decode.hip"],

@@ -79,7 +79,7 @@ Plan make_plan(const moe_problem& p) {
   if (!decode_capable(p)) decode = false;
   pl.path = decode ? kDecode : kGrouped;
   if (decode) pl.bm = decode_bm();
-  else pl.bm = p.weight_dtype == MOE_F32 ? gateup_f32_bm() : grouped_mfma_bm();
+  else pl.bm = p.weight_dtype == MOE_F32 ? gateup_f32_bm() : (is_fp8(p) ? grouped_fp8_bm() : grouped_mfma_bm());
   return pl;
 }
 
@@ -210,7 +210,7 @@ moe_status moe_plan_describe(const moe_problem* p, char* buf, size_t len) {
   const char* sname = p->scale_fmt == MOE_SCALE_F32 ? "f32" : (p->scale_fmt == MOE_SCALE_UE8M0 ? "ue8m0" : "none");
   const char* kern = pl.path == kDecode ? "stream_weights_16tok_mfma16x16x32"
                      : p->weight_dtype == MOE_F32 ? "fma_64x64"
-                     : p->weight_dtype == MOE_BF16 ? "mfma32x32x16_bf16_256x256_dma_ring4"
+                     : p->weight_dtype == MOE_BF16 ? "mfma32x32x16_bf16_128x256_ldsA_regB"
                                                    : "gateup_mfma32x32x16_on_widened_e4m3_256x128+down_mfma16x16x128_e4m3_256x256";
   snprintf(buf, len, "path=%s weights=%s scales=%s kernels=%s combine=%s workspace_bytes=%zu",
            pl.path == kDecode ? "decode" : "grouped", wname, sname, kern,

@@ -1,0 +1,311 @@
+// bf16 grouped GEMMs of the experts forward on MFMA (gfx950).
+//
+// The Experts backends page (backend table, "grouped_mm" row) sorts the tokens by
+// selected expert and projects them in one grouped GEMM; the expert is the gated
+// MLP of the "deepgemm_megamoe" row and the "SonicMoE" section (up projection,
+// SwiGLU, down projection).  Two kernels share one main loop:
+//
+//   gate_up : rows = hidden rows gathered through the sorted permutation, weights
+//             W_gate_up[e] ([2I, H], K = H contiguous).  The weight tile holds 128 gate
+//             rows and the matching 128 up rows, and every wave owns both halves of
+//             its output columns, so a = silu(gate) * up is formed in registers and
+//             stored once as bf16.
+//   down    : rows = the SwiGLU rows (already in sorted order), weights W_down[e]
+//             ([H, I], K = I contiguous).  The epilogue scales each row by its routing
+//             weight and adds it into the token's float32 output row (hardware float
+//             atomics), or stores it to the slot's own row for the deterministic combine.
+//
+// A workgroup of eight waves (two per SIMD, so one wave's LDS and barrier waits are
+// covered by the other's MFMAs) computes a 256-row x 256-column tile with 32x32x16
+// MFMA.  The waves form a 2 x 4 grid of 128 x 64 wave tiles (eight 32x32 float32
+// accumulator fragments each); the rows of wave (wm, wn) are the 32-row fragments
+// wm, wm + 2, wm + 4, wm + 6 of the tile, so a partly filled tile spreads its work over
+// both waves of every SIMD.
+//
+// K advances in slices of 64 elements (one 128-byte L2 line of every operand row) held
+// in a two-slot LDS ring filled by global->LDS DMA: slice kt + 1 is loaded while slice kt
+// is multiplied, and one barrier per slice publishes a slice and frees the slot of the
+// previous one.  In a slot a tile row is 128 bytes whose eight 16-byte chunks
+// are XOR-permuted by (row >> 1) & 7, so the 16 rows read by each 16-lane group of a
+// fragment load hit distinct banks.  A rows past the tile's last 32-row fragment are
+// neither loaded nor multiplied.
+//
+// Work items are (expert, N tile, M tile) with M fastest; an expert's rows are split
+// evenly over its M tiles (multiples of 32 rows, at most 256).  The grid is persistent
+// and each round hands every XCD (blockIdx % 8) a contiguous run of items, so the M tiles
+// sharing a weight tile run at the same pace on one XCD and meet in its L2.  The expert
+// tables live in LDS.
+#include <type_traits>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 512;             // eight waves, two per SIMD, in a 2 x 4 grid
+constexpr int NW = 8;
+constexpr int BM = 256;                   // tile rows
+constexpr int BN = 256;                   // tile columns (= weight rows)
+constexpr int MFRAG = 4;                  // 32-row fragments per wave (interleaved)
+constexpr int NFRAG = 2;                  // 32-column fragments per wave
+constexpr int KS = 64;                    // K elements per slice
+constexpr int ROWB = KS * 2;              // bytes of one tile row in one slice
+constexpr int KSTEPS = KS / 16;           // 32x32x16 k steps per slice
+constexpr int NSTAGE = 2;                 // ring slots
+constexpr int STAGE = (BM + BN) * ROWB;   // 64 KB: A rows, then B rows
+constexpr int RPI = 1024 / ROWB;          // tile rows per DMA instruction (1 KB)
+constexpr int ALD = BM / RPI / NW;        // most A DMA instructions per wave per slice
+constexpr int BLD = BN / RPI / NW;        // B DMA instructions per wave per slice
+constexpr int kMaxE = 1024;
+
+enum { kGateUp = 0, kDownAtomic = 1, kDownSlots = 2 };
+
+// LDS chunk slot of logical 16-byte chunk c of tile row `row`: the 16 rows of a 16-lane
+// fragment-read group land in 16 distinct 16-byte bank groups of a 256-byte window
+__device__ __forceinline__ int chunk_slot(int row, int c) { return c ^ ((row >> 1) & 7); }
+
+template <int MODE>
+__global__ __launch_bounds__(kThreads, 1) void grouped_bf16_kernel(GroupedArgs g) {
+  __shared__ __attribute__((aligned(1024))) char ring[NSTAGE][STAGE];
+  __shared__ int sMt[kMaxE + 1];
+  __shared__ int sOff[kMaxE + 1];
+  __shared__ int sTok[BM];    // epilogue: token (atomic combine) or slot (per-slot rows)
+  __shared__ float sWt[BM];   // epilogue: routing weight
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int hgrp = lane >> 5, r32 = lane & 31;
+  const int gx = gridDim.x >> 3;
+  const int xcd = blockIdx.x & 7, xslot = blockIdx.x >> 3;
+  const int E = g.E;
+  const int KT = g.K / KS;
+  const int ncols = MODE == kGateUp ? g.I : g.H;     // output columns of the whole GEMM
+  const char* __restrict__ Abase = static_cast<const char*>(g.a);
+  const uint32_t a_row_bytes = (uint32_t)(g.lda * 2);
+  const uint32_t b_row_bytes = (uint32_t)(g.K * 2);
+
+  for (int i = tid; i <= E; i += kThreads) {
+    sMt[i] = g.mt[i];
+    sOff[i] = g.offsets[i];
+  }
+  __syncthreads();
+  const int n_items = sMt[E] * g.NT;
+
+  // DMA lane L of the instruction for row block b (RPI rows) fills chunk slot (L & 7) of
+  // tile row RPI b + (L >> 3) with the global chunk chunk_slot maps there
+  const int ld_row = lane >> 3, ld_slot = lane & 7;
+  const uint32_t ring0 = lds_addr(&ring[0][0]);
+  // fragment reads (k step s): tile row base + r32 (base a multiple of 32), logical
+  // chunk 2 s + hgrp, at row * ROWB + (chunk_slot(row, 2 s + hgrp) << 4)
+  uint32_t foff[KSTEPS];
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) foff[s] = (uint32_t)(r32 * ROWB + (chunk_slot(r32, 2 * s + hgrp) << 4));
+
+  // tile column of this wave's fragment j (gate/up: fragment 0 holds the gate columns,
+  // fragment 1 the matching up columns, of output columns 32 wn .. 32 wn + 31)
+  auto tile_col0 = [&](int j) __attribute__((always_inline)) -> int {
+    if (MODE == kGateUp) return (j == 0 ? 0 : BN / 2) + wn * 32;
+    return wn * 64 + j * 32;
+  };
+
+  f32x16 acc[MFRAG][NFRAG];
+
+  for (int w = xcd * gx + xslot; w < n_items; w += gridDim.x) {
+    // ---- the tile of work item w
+    int e;
+    {
+      int lo = 0, hi = E - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (sMt[mid] * g.NT <= w) lo = mid; else hi = mid - 1;
+      }
+      e = lo;
+    }
+    const int mt_e = sMt[e + 1] - sMt[e];
+    const int local = w - sMt[e] * g.NT;
+    const int nt = local / mt_e;
+    const int mloc = local - nt * mt_e;
+    const int cnt = sOff[e + 1] - sOff[e];
+    const int per = min(BM, ((cnt + mt_e - 1) / mt_e + 31) & ~31);
+    const int row0 = sOff[e] + mloc * per;
+    const int rows = min(per, sOff[e + 1] - row0);
+    if (rows <= 0) continue;   // (never: the even split leaves every M tile some rows)
+    const char* __restrict__ Bexp = static_cast<const char*>(g.b) + (int64_t)e * g.b_expert_stride * 2;
+
+    // global weight row of tile column c; columns past the matrix repeat its last row
+    auto b_row = [&](int c) __attribute__((always_inline)) -> int {
+      if (MODE == kGateUp) {
+        const int i = min(nt * (BN / 2) + (c % (BN / 2)), g.I - 1);
+        return c < BN / 2 ? i : g.I + i;
+      }
+      return min(nt * BN + c, g.H - 1);
+    };
+    auto a_src = [&](int r) __attribute__((always_inline)) -> int {   // source row of tile row r
+      const int p = row0 + min(r, rows - 1);                          // (rows past the end repeat the last)
+      return g.a_rows ? g.a_rows[p] / g.a_row_div : p;
+    };
+
+    // epilogue inputs of the down projection (consumed after the K loop)
+    int my_tok = 0;
+    float my_wt = 0.f;
+    if (MODE != kGateUp && tid < rows) {
+      const int slot = g.perm[row0 + tid];
+      my_tok = MODE == kDownAtomic ? slot / g.k : slot;
+      my_wt = g.topk_w[slot];
+    }
+
+    // DMA: wave w loads row blocks w, w + 8, ... of A (those covering the tile's 32-row
+    // fragments) and of B.  32-bit byte offsets: operands are < 4 GiB (checked on the host).
+    const int nfr = (rows + 31) / 32;           // 32-row fragments with rows
+    const int nblk = nfr * (32 / RPI);          // A row blocks to load
+    uint32_t aoff[ALD], boff[BLD];
+#pragma unroll
+    for (int q = 0; q < ALD; ++q) {
+      const int r = RPI * (wave + NW * q) + ld_row;
+      aoff[q] = (uint32_t)a_src(r) * a_row_bytes + (uint32_t)(chunk_slot(r, ld_slot) << 4);
+    }
+#pragma unroll
+    for (int q = 0; q < BLD; ++q) {
+      const int c = RPI * (wave + NW * q) + ld_row;
+      boff[q] = (uint32_t)b_row(c) * b_row_bytes + (uint32_t)(chunk_slot(c, ld_slot) << 4);
+    }
+    // DMA of K slice kt into ring slot kt % 2
+    auto issue = [&](int kt) __attribute__((always_inline)) {
+      const uint32_t st = ring0 + (uint32_t)((kt & 1) * STAGE);
+      const char* ab = Abase + (int64_t)kt * ROWB;
+      const char* bb = Bexp + (int64_t)kt * ROWB;
+#pragma unroll
+      for (int q = 0; q < ALD; ++q)
+        if (wave + NW * q < nblk) dma_lds_x4(ab, aoff[q], st + (uint32_t)((wave + NW * q) * 1024));
+#pragma unroll
+      for (int q = 0; q < BLD; ++q) dma_lds_x4(bb, boff[q], st + (uint32_t)(BM * ROWB + (wave + NW * q) * 1024));
+    };
+
+#pragma unroll
+    for (int i = 0; i < MFRAG; ++i) {
+#pragma unroll
+      for (int j = 0; j < NFRAG; ++j) acc[i][j] = f32x16{};
+    }
+
+    // multiply slice kt (ring slot kt % 2) on the NI active fragments of this wave
+    auto compute = [&](auto NI_, int kt) __attribute__((always_inline)) {
+      constexpr int NI = decltype(NI_)::value;
+      const char* As = &ring[kt & 1][0];
+      const char* Bs = As + BM * ROWB;
+      bf16x8 fa[2][NI > 0 ? NI : 1], fb[2][NFRAG];
+      auto load_frags = [&](int s, int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+          fa[buf][i] = *reinterpret_cast<const bf16x8*>(As + (2 * i + wm) * 32 * ROWB + foff[s]);
+#pragma unroll
+        for (int j = 0; j < NFRAG; ++j)
+          fb[buf][j] = *reinterpret_cast<const bf16x8*>(Bs + tile_col0(j) * ROWB + foff[s]);
+      };
+      if constexpr (NI > 0) load_frags(0, 0);
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) {
+        if constexpr (NI > 0) {
+          if (s + 1 < KSTEPS) load_frags(s + 1, (s + 1) & 1);
+#pragma unroll
+          for (int i = 0; i < NI; ++i) {
+#pragma unroll
+            for (int j = 0; j < NFRAG; ++j) acc[i][j] = mfma_32x32x16_bf16(fa[s & 1][i], fb[s & 1][j], acc[i][j]);
+          }
+        }
+      }
+    };
+    auto kloop = [&](auto NI_) __attribute__((always_inline)) {
+      issue(0);
+      for (int kt = 0; kt < KT; ++kt) {
+        wait_vmcnt<0>();      // this wave's part of slice kt has landed ...
+        __syncthreads();      // ... and so has everyone's; slot (kt + 1) % 2 is free
+        if (kt + 1 < KT) issue(kt + 1);
+        compute(NI_, kt);
+      }
+    };
+    // this wave's fragments 2 i + wm with rows: i < NI
+    switch ((nfr - wm + 1) / 2) {
+      case 4: kloop(std::integral_constant<int, 4>{}); break;
+      case 3: kloop(std::integral_constant<int, 3>{}); break;
+      case 2: kloop(std::integral_constant<int, 2>{}); break;
+      case 1: kloop(std::integral_constant<int, 1>{}); break;
+      default: kloop(std::integral_constant<int, 0>{}); break;
+    }
+    __syncthreads();   // every wave is done with the ring
+
+    // ---- epilogue.  32x32 fragment (i, j): element v at tile row (2 i + wm) * 32 +
+    // 8 (v / 4) + 4 hgrp + (v % 4), tile column tile_col0(j) + r32
+    if constexpr (MODE == kGateUp) {
+      // a = silu(gate) * up as bf16, staged through LDS as [BM rows][128 columns] and
+      // written to HBM in 16-byte row pieces
+      uint16_t* stage = reinterpret_cast<uint16_t*>(&ring[0][0]);
+#pragma unroll
+      for (int i = 0; i < MFRAG; ++i) {
+        if ((2 * i + wm) * 32 >= rows) break;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = (2 * i + wm) * 32 + 8 * (v >> 2) + 4 * hgrp + (v & 3);
+          const float a = silu_fast(acc[i][0][v]) * acc[i][1][v];
+          stage[r * 128 + wn * 32 + r32] = (uint16_t)f32_to_bf16_bits(a);
+        }
+      }
+      __syncthreads();
+      uint16_t* out = static_cast<uint16_t*>(g.act_out);
+      for (int c = tid; c < rows * 16; c += kThreads) {
+        const int r = c >> 4, piece = c & 15;
+        const int col = nt * 128 + piece * 8;
+        if (col < ncols)
+          *reinterpret_cast<i32x4*>(out + (int64_t)(row0 + r) * g.I + col) =
+              *reinterpret_cast<const i32x4*>(stage + r * 128 + piece * 8);
+      }
+    } else {
+      if (tid < BM) {
+        sTok[tid] = my_tok;
+        sWt[tid] = my_wt;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < MFRAG; ++i) {
+        if ((2 * i + wm) * 32 >= rows) break;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = (2 * i + wm) * 32 + 8 * (v >> 2) + 4 * hgrp + (v & 3);
+          if (r >= rows) continue;
+          const float wt = sWt[r];
+          const int64_t tok = sTok[r];
+#pragma unroll
+          for (int j = 0; j < NFRAG; ++j) {
+            const int col = nt * BN + tile_col0(j) + r32;
+            if (col < ncols) {
+              if (MODE == kDownAtomic) unsafeAtomicAdd(g.acc_out + tok * g.H + col, wt * acc[i][j][v]);
+              else g.slot_out[tok * g.H + col] = wt * acc[i][j][v];
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();   // the staging area and sTok / sWt are reused by the next item
+  }
+}
+
+template <int MODE>
+hipError_t launch(const GroupedArgs& g, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((grouped_bf16_kernel<MODE>), dim3(grid), dim3(kThreads), 0, s, g);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int grouped_mfma_bm() { return BM; }
+int gateup_bf16_cols() { return BN / 2; }
+int down_bf16_cols() { return BN; }
+
+hipError_t launch_gateup_bf16(const GroupedArgs& g, int grid, hipStream_t s) { return launch<kGateUp>(g, grid, s); }
+
+hipError_t launch_down_bf16(const GroupedArgs& g, int grid, hipStream_t s) {
+  return g.slot_out ? launch<kDownSlots>(g, grid, s) : launch<kDownAtomic>(g, grid, s);
+}
+
+}  // namespace moe

@@ -416,6 +416,7 @@ hipError_t launch(const GroupedArgs& g, int grid, hipStream_t s) {
 
 }  // namespace
 
+int grouped_fp8_bm() { return BM; }
 int gateup_fp8_cols() { return Cfg<kOpFp8Wide>::BN / 2; }
 int down_fp8_cols() { return Cfg<kOpFp8>::BN; }
 

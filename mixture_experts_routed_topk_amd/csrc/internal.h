@@ -63,13 +63,14 @@ struct GroupedArgs {
 inline int64_t max_mtiles(int64_t A, int E, int bm) { return A / bm + (A < E ? A : E); }
 
 // bf16 MFMA grouped GEMMs (persistent grid, LDS ring filled by DMA)
-int grouped_mfma_bm();            // tile height of the bf16 and e4m3 grouped GEMMs
+int grouped_mfma_bm();            // tile height of the bf16 grouped GEMMs
 int gateup_bf16_cols();           // SwiGLU columns per N tile of the gate/up kernel
 int down_bf16_cols();             // hidden columns per N tile of the down kernel
 hipError_t launch_gateup_bf16(const GroupedArgs& g, int grid, hipStream_t s);
 hipError_t launch_down_bf16(const GroupedArgs& g, int grid, hipStream_t s);
 
-// e4m3 (128x128 block-scaled) MFMA grouped GEMMs (persistent grid, same tile height)
+// e4m3 (128x128 block-scaled) MFMA grouped GEMMs (persistent grid)
+int grouped_fp8_bm();
 int gateup_fp8_cols();
 int down_fp8_cols();
 hipError_t launch_gateup_fp8(const GroupedArgs& g, int grid, hipStream_t s);
