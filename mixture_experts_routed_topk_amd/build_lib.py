@@ -29,9 +29,6 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
     "-Wno-unused-command-line-argument",
-    # the bf16 grouped GEMM names registers above the compiler's VGPR budget in its asm
-    # clobber lists on purpose (they hold its B operands)
-    "-Wno-inline-asm",
 ]
 
 
