@@ -89,17 +89,23 @@ __device__ __forceinline__ f32x16 mfma_32x32x64_e4m3(i32x8 a, i32x8 b, f32x16 c)
 // The compiler does not count these loads: every reader of the data waits for them
 // with wait_vmcnt<N>() (at most N vector-memory operations of this wave outstanding,
 // which retire in issue order) followed by a workgroup barrier.
+//
+// The compiler's hazard checks do not look inside inline asm, so each load carries its
+// own wait states: on the gfx9 family a VMEM instruction that reads an SGPR written by
+// a VALU instruction (v_readlane / v_readfirstlane, as when the compiler restores a
+// spilled SGPR) needs 5 wait states, and an LDS DMA needs 1 after an SALU write of M0.
+// Without them the load can use a stale base address.  s_nop 4 provides 5.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 __device__ __forceinline__ void dma_lds_x4(const void* base, uint32_t off, uint32_t m0) {
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(m0) : "memory");
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(m0) : "memory");
 }
 __device__ __forceinline__ void dma_lds_x1(const void* base, uint32_t off, uint32_t m0) {
-  asm volatile("global_load_lds_dword %0, %1" ::"v"(off), "s"(base), "{m0}"(m0) : "memory");
+  asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "{m0}"(m0) : "memory");
 }
 __device__ __forceinline__ void dma_lds_u8(const void* base, uint32_t off, uint32_t m0) {
-  asm volatile("global_load_lds_ubyte %0, %1" ::"v"(off), "s"(base), "{m0}"(m0) : "memory");
+  asm volatile("s_nop 4\n\tglobal_load_lds_ubyte %0, %1" ::"v"(off), "s"(base), "{m0}"(m0) : "memory");
 }
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
