@@ -16,25 +16,27 @@
 //             atomics), or stores it to the slot's own row for the deterministic combine.
 //
 // A workgroup of eight waves (two per SIMD, so one wave's LDS and barrier waits are
-// covered by the other's MFMAs) computes a 256-row x 256-column tile with 32x32x16
-// MFMA.  The waves form a 2 x 4 grid of 128 x 64 wave tiles (eight 32x32 float32
-// accumulator fragments each); the rows of wave (wm, wn) are the 32-row fragments
-// wm, wm + 2, wm + 4, wm + 6 of the tile, so a partly filled tile spreads its work over
-// both waves of every SIMD.
+// covered by the other's MFMAs) computes a tile of up to 160 rows x 256 columns with
+// 32x32x16 MFMA.  The waves form a 2 x 4 grid of wave tiles of up to three 32-row x two
+// 32-column fragments; the rows of wave (wm, wn) are the 32-row fragments wm, wm + 2,
+// wm + 4 of the tile, so a partly filled tile spreads its work over both waves of every
+// SIMD.
 //
 // K advances in slices of 64 elements (one 128-byte L2 line of every operand row) held
-// in a two-slot LDS ring filled by global->LDS DMA: slice kt + 1 is loaded while slice kt
-// is multiplied, and one barrier per slice publishes a slice and frees the slot of the
-// previous one.  In a slot a tile row is 128 bytes whose eight 16-byte chunks
-// are XOR-permuted by (row >> 1) & 7, so the 16 rows read by each 16-lane group of a
-// fragment load hit distinct banks.  A rows past the tile's last 32-row fragment are
-// neither loaded nor multiplied.
+// in a three-slot LDS ring (52 KB per slot) filled by global->LDS DMA.  Slices kt + 1 and
+// kt + 2 stream in while slice kt is multiplied: the DMA of slice kt + 2 is spread over
+// the four k steps of slice kt, one A and one B block per step, into the slot that
+// slice kt - 1 used.  One barrier per slice publishes a slice and frees that slot.  In a
+// slot a tile row is 128 bytes whose eight 16-byte chunks are XOR-permuted by
+// (row >> 1) & 7, so the 16 rows read by each 16-lane group of a fragment load hit
+// distinct banks.  A rows past the tile's last 32-row fragment are neither loaded nor
+// multiplied.
 //
 // Work items are (expert, N tile, M tile) with M fastest; an expert's rows are split
-// evenly over its M tiles (multiples of 32 rows, at most 256).  The grid is persistent
+// evenly over its M tiles (multiples of 32 rows, at most 160).  The grid is persistent
 // and each round hands every XCD (blockIdx % 8) a contiguous run of items, so the M tiles
-// sharing a weight tile run at the same pace on one XCD and meet in its L2.  The expert
-// tables live in LDS.
+// sharing a weight tile run at the same pace on one XCD and meet in its L2.  The M-tile
+// table lives in LDS as 16-bit entries (read from global memory when it does not fit).
 #include <type_traits>
 
 #include "device_common.h"
@@ -45,19 +47,20 @@ namespace {
 
 constexpr int kThreads = 512;             // eight waves, two per SIMD, in a 2 x 4 grid
 constexpr int NW = 8;
-constexpr int BM = 256;                   // tile rows
+constexpr int BM = 160;                   // tile rows (five 32-row fragments)
 constexpr int BN = 256;                   // tile columns (= weight rows)
-constexpr int MFRAG = 4;                  // 32-row fragments per wave (interleaved)
+constexpr int MFRAG = 3;                  // 32-row fragments per wave (2 i + wm < 5)
 constexpr int NFRAG = 2;                  // 32-column fragments per wave
 constexpr int KS = 64;                    // K elements per slice
 constexpr int ROWB = KS * 2;              // bytes of one tile row in one slice
 constexpr int KSTEPS = KS / 16;           // 32x32x16 k steps per slice
-constexpr int NSTAGE = 2;                 // ring slots
-constexpr int STAGE = (BM + BN) * ROWB;   // 64 KB: A rows, then B rows
+constexpr int NSTAGE = 3;                 // ring slots
+constexpr int STAGE = (BM + BN) * ROWB;   // 52 KB: A rows, then B rows
 constexpr int RPI = 1024 / ROWB;          // tile rows per DMA instruction (1 KB)
-constexpr int ALD = BM / RPI / NW;        // most A DMA instructions per wave per slice
+constexpr int ALD = (BM / RPI + NW - 1) / NW;   // most A DMA instructions per wave per slice
 constexpr int BLD = BN / RPI / NW;        // B DMA instructions per wave per slice
 constexpr int kMaxE = 1024;
+static_assert(ALD <= KSTEPS && BLD == KSTEPS, "the DMA of a slice is spread one A and one B block per k step");
 
 enum { kGateUp = 0, kDownAtomic = 1, kDownSlots = 2 };
 
@@ -68,8 +71,7 @@ __device__ __forceinline__ int chunk_slot(int row, int c) { return c ^ ((row >> 
 template <int MODE>
 __global__ __launch_bounds__(kThreads, 1) void grouped_bf16_kernel(GroupedArgs g) {
   __shared__ __attribute__((aligned(1024))) char ring[NSTAGE][STAGE];
-  __shared__ int sMt[kMaxE + 1];
-  __shared__ int sOff[kMaxE + 1];
+  __shared__ uint16_t sMt[kMaxE + 1];   // M-tile starts (when they fit in 16 bits)
   __shared__ int sTok[BM];    // epilogue: token (atomic combine) or slot (per-slot rows)
   __shared__ float sWt[BM];   // epilogue: routing weight
 
@@ -86,12 +88,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_bf16_kernel(GroupedArgs g
   const uint32_t a_row_bytes = (uint32_t)(g.lda * 2);
   const uint32_t b_row_bytes = (uint32_t)(g.K * 2);
 
-  for (int i = tid; i <= E; i += kThreads) {
-    sMt[i] = g.mt[i];
-    sOff[i] = g.offsets[i];
-  }
+  const int n_mt = g.mt[E];
+  const bool mt_lds = n_mt < 65536;
+  if (mt_lds)
+    for (int i = tid; i <= E; i += kThreads) sMt[i] = (uint16_t)g.mt[i];
   __syncthreads();
-  const int n_items = sMt[E] * g.NT;
+  const int n_items = n_mt * g.NT;
+  auto mt_at = [&](int i) __attribute__((always_inline)) -> int { return mt_lds ? (int)sMt[i] : g.mt[i]; };
 
   // DMA lane L of the instruction for row block b (RPI rows) fills chunk slot (L & 7) of
   // tile row RPI b + (L >> 3) with the global chunk chunk_slot maps there
@@ -119,18 +122,20 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_bf16_kernel(GroupedArgs g
       int lo = 0, hi = E - 1;
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (sMt[mid] * g.NT <= w) lo = mid; else hi = mid - 1;
+        if (mt_at(mid) * g.NT <= w) lo = mid; else hi = mid - 1;
       }
       e = lo;
     }
-    const int mt_e = sMt[e + 1] - sMt[e];
-    const int local = w - sMt[e] * g.NT;
+    const int mt0 = mt_at(e);
+    const int mt_e = mt_at(e + 1) - mt0;
+    const int local = w - mt0 * g.NT;
     const int nt = local / mt_e;
     const int mloc = local - nt * mt_e;
-    const int cnt = sOff[e + 1] - sOff[e];
+    const int off0 = g.offsets[e], off1 = g.offsets[e + 1];
+    const int cnt = off1 - off0;
     const int per = min(BM, ((cnt + mt_e - 1) / mt_e + 31) & ~31);
-    const int row0 = sOff[e] + mloc * per;
-    const int rows = min(per, sOff[e + 1] - row0);
+    const int row0 = off0 + mloc * per;
+    const int rows = min(per, off1 - row0);
     if (rows <= 0) continue;   // (never: the even split leaves every M tile some rows)
     const char* __restrict__ Bexp = static_cast<const char*>(g.b) + (int64_t)e * g.b_expert_stride * 2;
 
@@ -171,17 +176,33 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_bf16_kernel(GroupedArgs g
       const int c = RPI * (wave + NW * q) + ld_row;
       boff[q] = (uint32_t)b_row(c) * b_row_bytes + (uint32_t)(chunk_slot(c, ld_slot) << 4);
     }
-    // DMA of K slice kt into ring slot kt % 2
-    auto issue = [&](int kt) __attribute__((always_inline)) {
-      const uint32_t st = ring0 + (uint32_t)((kt & 1) * STAGE);
-      const char* ab = Abase + (int64_t)kt * ROWB;
-      const char* bb = Bexp + (int64_t)kt * ROWB;
-#pragma unroll
-      for (int q = 0; q < ALD; ++q)
-        if (wave + NW * q < nblk) dma_lds_x4(ab, aoff[q], st + (uint32_t)((wave + NW * q) * 1024));
-#pragma unroll
-      for (int q = 0; q < BLD; ++q) dma_lds_x4(bb, boff[q], st + (uint32_t)(BM * ROWB + (wave + NW * q) * 1024));
+    // DMA of this wave's part p of K slice kt into ring slot `slot`: A block q = p (if it
+    // covers rows of the tile) and B block q = p
+    auto issue_part = [&](int kt, int slot, int p) __attribute__((always_inline)) {
+      const uint32_t st = ring0 + (uint32_t)(slot * STAGE);
+      if (p < ALD && wave + NW * p < nblk)
+        dma_lds_x4(Abase + (int64_t)kt * ROWB, aoff[p < ALD ? p : 0], st + (uint32_t)((wave + NW * p) * 1024));
+      dma_lds_x4(Bexp + (int64_t)kt * ROWB, boff[p], st + (uint32_t)(BM * ROWB + (wave + NW * p) * 1024));
     };
+    auto issue = [&](int kt, int slot) __attribute__((always_inline)) {
+#pragma unroll
+      for (int p = 0; p < KSTEPS; ++p) issue_part(kt, slot, p);
+    };
+    // vector-memory instructions this wave issues per slice
+    int na = 0;
+#pragma unroll
+    for (int q = 0; q < ALD; ++q) na += wave + NW * q < nblk ? 1 : 0;
+    const int nld = __builtin_amdgcn_readfirstlane(na + BLD);
+    // wait until this wave has at most one slice (nld instructions) in flight
+    auto wait_one_slice = [&]() __attribute__((always_inline)) {
+      switch (nld) {
+        case BLD: wait_vmcnt<BLD>(); break;
+        case BLD + 1: wait_vmcnt<BLD + 1>(); break;
+        case BLD + 2: wait_vmcnt<BLD + 2>(); break;
+        default: wait_vmcnt<BLD + 3>(); break;
+      }
+    };
+    static_assert(ALD <= 3, "wait_one_slice covers at most three A blocks per wave");
 
 #pragma unroll
     for (int i = 0; i < MFRAG; ++i) {
@@ -189,10 +210,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_bf16_kernel(GroupedArgs g
       for (int j = 0; j < NFRAG; ++j) acc[i][j] = f32x16{};
     }
 
-    // multiply slice kt (ring slot kt % 2) on the NI active fragments of this wave
-    auto compute = [&](auto NI_, int kt) __attribute__((always_inline)) {
+    // multiply slice kt (ring slot `slot`) on the NI active fragments of this wave; with
+    // `next`, slice kt + 2 is issued into slot `nslot` one part per k step
+    auto compute = [&](auto NI_, int slot, bool next, int kt2, int nslot) __attribute__((always_inline)) {
       constexpr int NI = decltype(NI_)::value;
-      const char* As = &ring[kt & 1][0];
+      const char* As = &ring[slot][0];
       const char* Bs = As + BM * ROWB;
       bf16x8 fa[2][NI > 0 ? NI : 1], fb[2][NFRAG];
       auto load_frags = [&](int s, int buf) __attribute__((always_inline)) {
@@ -214,20 +236,25 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_bf16_kernel(GroupedArgs g
             for (int j = 0; j < NFRAG; ++j) acc[i][j] = mfma_32x32x16_bf16(fa[s & 1][i], fb[s & 1][j], acc[i][j]);
           }
         }
+        if (next) issue_part(kt2, nslot, s);
       }
     };
+    // three-slot ring: slices kt + 1 and kt + 2 stream in while slice kt is multiplied
     auto kloop = [&](auto NI_) __attribute__((always_inline)) {
-      issue(0);
+      issue(0, 0);
+      if (1 < KT) issue(1, 1);
+      int slot = 0;
       for (int kt = 0; kt < KT; ++kt) {
-        wait_vmcnt<0>();      // this wave's part of slice kt has landed ...
-        __syncthreads();      // ... and so has everyone's; slot (kt + 1) % 2 is free
-        if (kt + 1 < KT) issue(kt + 1);
-        compute(NI_, kt);
+        if (kt + 1 < KT) wait_one_slice();   // slice kt has landed (kt + 1 may not) ...
+        else wait_vmcnt<0>();
+        __syncthreads();                     // ... for every wave; slot (kt + 2) % 3 is free
+        const int nslot = slot == 0 ? 2 : slot - 1;
+        compute(NI_, slot, kt + 2 < KT, kt + 2, nslot);
+        slot = slot == 2 ? 0 : slot + 1;
       }
     };
     // this wave's fragments 2 i + wm with rows: i < NI
     switch ((nfr - wm + 1) / 2) {
-      case 4: kloop(std::integral_constant<int, 4>{}); break;
       case 3: kloop(std::integral_constant<int, 3>{}); break;
       case 2: kloop(std::integral_constant<int, 2>{}); break;
       case 1: kloop(std::integral_constant<int, 1>{}); break;
