@@ -87,6 +87,7 @@ Plan make_plan(const moe_problem& p) {
 
 struct Layout {
   size_t bad, counts, offsets, mt, perm, inv;
+  size_t route_part; // chunked routing: per-chunk expert counts [G][E] and bad-id counts [G]
   size_t act;        // SwiGLU rows [A][I]: f32 (f32 weights, and fp8 before quantising) or bf16
   size_t act_q;      // fp8: e4m3 SwiGLU rows [A][I]
   size_t act_s;      // fp8: their scales [A][I/128]
@@ -111,6 +112,7 @@ Layout make_layout(const moe_problem& p) {
   L.mt = take(4 * (E + 1));
   L.perm = take(4 * A);
   L.inv = take(4 * A);
+  L.route_part = take(4 * (E + 1) * (size_t)kRouteMaxChunks);
   const bool fp8 = p.weight_dtype == MOE_FP8_E4M3;
   L.act = take((p.weight_dtype == MOE_BF16 ? 2 : 4) * A * I);
   L.act_q = fp8 ? take(A * I) : o;
@@ -244,6 +246,7 @@ moe_status moe_route(const moe_problem* p, const int32_t* topk_idx, int32_t* cou
   r.perm = perm;
   r.inv = inv;
   r.bad = reinterpret_cast<int32_t*>(ws + L.bad);
+  r.part = reinterpret_cast<int32_t*>(ws + L.route_part);
   MOE_HIP_CHECK(launch_route(r, s));
   if (p->flags & MOE_FLAG_CHECK_INDICES) {
     int32_t bad = 0;
@@ -292,7 +295,10 @@ moe_status moe_experts_forward(const moe_problem* p, const void* hidden, const i
   float* acc = det ? nullptr : reinterpret_cast<float*>(ws + L.acc);
   float* slots = det ? reinterpret_cast<float*>(ws + L.slots) : nullptr;
 
-  if (!det) {
+  // the atomic combine adds into a cleared float32 accumulator; the bf16 grouped
+  // gate_up kernel clears it itself after its tiles, other paths launch a fill
+  const bool zero_in_gateup = !det && pl.path != kDecode && p->weight_dtype == MOE_BF16;
+  if (!det && !zero_in_gateup) {
     MOE_HIP_CHECK(stage_mark(MOE_STAGE_ZERO, 0, s));
     MOE_HIP_CHECK(launch_zero_f32(acc, p->T * (int64_t)p->H, s));
     MOE_HIP_CHECK(stage_mark(MOE_STAGE_ZERO, 1, s));
@@ -310,6 +316,7 @@ moe_status moe_experts_forward(const moe_problem* p, const void* hidden, const i
   r.bad = bad;
   r.bm0 = pl.bm;
   r.mt0 = mt;
+  r.part = reinterpret_cast<int32_t*>(ws + L.route_part);
   MOE_HIP_CHECK(stage_mark(MOE_STAGE_ROUTE, 0, s));
   MOE_HIP_CHECK(launch_route(r, s));
   MOE_HIP_CHECK(stage_mark(MOE_STAGE_ROUTE, 1, s));
@@ -340,6 +347,10 @@ moe_status moe_experts_forward(const moe_problem* p, const void* hidden, const i
   gu.b_expert_stride = 2 * (int64_t)p->I * p->H;
   gu.K = p->H;
   gu.act_out = ws + L.act;
+  if (zero_in_gateup) {
+    gu.zero_out = acc;
+    gu.zero_n4 = p->T * (int64_t)p->H / 4;   // H is a multiple of 128
+  }
   // down + routing weight + combine: rows = SwiGLU rows in sorted order
   GroupedArgs dn = g;
   dn.a = fp8 ? (const void*)(ws + L.act_q) : (const void*)(ws + L.act);

@@ -315,6 +315,18 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_bf16_kernel(GroupedArgs g
     }
     __syncthreads();   // the staging area and sTok / sWt are reused by the next item
   }
+  // gate_up also clears the float32 accumulator of the down kernel's combine: each
+  // workgroup a contiguous share, after its last tile (workgroups with one tile fewer
+  // do it while the others finish)
+  if constexpr (MODE == kGateUp) {
+    if (g.zero_out != nullptr) {
+      const int64_t per = (g.zero_n4 + gridDim.x - 1) / gridDim.x;
+      const int64_t z0 = per * blockIdx.x;
+      const int64_t z1 = min(g.zero_n4, z0 + per);
+      f32x4* z = reinterpret_cast<f32x4*>(g.zero_out);
+      for (int64_t i = z0 + tid; i < z1; i += kThreads) z[i] = f32x4{};
+    }
+  }
 }
 
 template <int MODE>

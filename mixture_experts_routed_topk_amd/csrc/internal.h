@@ -22,8 +22,17 @@ struct RouteArgs {
   int32_t* mt0;        // [E+1]
   int bm1;
   int32_t* mt1;
+  // batches of more than kRouteOneBlockMax slots are routed in route_chunks(A) chunks of
+  // route_chunk(A) slots; part holds (E + 1) * route_chunks(A) ints of scratch (when
+  // null, one workgroup routes the whole batch)
+  int32_t* part;
+  int chunk;           // (set by launch_route)
 };
+constexpr int kRouteOneBlockMax = 4096;
+constexpr int kRouteMaxChunks = 64;
 size_t route_lds_bytes(int E);
+int route_chunks(int A);
+int route_chunk(int A);
 hipError_t launch_route(const RouteArgs& args, hipStream_t stream);
 
 // ---------------------------------------------------------------------------- grouped GEMMs
@@ -57,6 +66,10 @@ struct GroupedArgs {
   int H;
   float* acc_out;           // [T][H] float32 accumulator (atomic combine), or
   float* slot_out;          // [A][H] float32 per-slot rows (deterministic combine)
+  // bf16 gate_up only: clear zero_n4 float4s at zero_out after its last tile (the
+  // accumulator the down kernel adds into), or nothing when zero_out is null
+  float* zero_out;
+  int64_t zero_n4;
 };
 
 // Upper bound on M tiles for a tile height (host-side grid sizing).

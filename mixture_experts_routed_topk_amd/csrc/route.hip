@@ -4,12 +4,20 @@
 // sorts tokens by their selected expert before one grouped GEMM; this is that sort
 // of the T*k (token, slot) pairs, done as a counting sort.
 //
-// One workgroup of 512 threads (8 waves).  Wave w owns a contiguous range of slots;
-// per-wave histograms live in LDS, so the placement of slot a is
+// Small batches run in one workgroup of 512 threads (8 waves).  Wave w owns a
+// contiguous range of slots; per-wave histograms live in LDS, so the placement of slot
+// a is
 //     offsets[e] + (slots of e in earlier waves) + (slots of e earlier in this wave),
 // which keeps equal experts in slot order.  Inside a wave, lanes holding the same
 // expert are found with one ballot per bit of the expert id (a multi-split), so a
 // 64-slot piece is ranked without atomics.
+//
+// Larger batches are split into G contiguous chunks of slots, one workgroup each, in
+// two launches: the first writes every chunk's per-expert counts to a [G][E] table in
+// the workspace; the second has every chunk read that table (its experts' totals and
+// the counts of earlier chunks), so slot a of chunk g lands at
+//     offsets[e] + (slots of e in chunks before g) + (its rank inside chunk g),
+// ranked as above.  Chunk 0 also writes the offsets, counts and M-tile tables.
 #include "device_common.h"
 #include "internal.h"
 
@@ -165,13 +173,194 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs p) {
   }
 }
 
+// ---------------------------------------------------------------------------- chunked
+// Per-wave counts of the ids in [beg, end) (this wave's part of the chunk) into
+// hist[wave][*]; returns the number of out-of-range ids this lane saw.
+__device__ int wave_histogram(const RouteArgs& p, int beg, int end, int32_t* hist) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int nbad = 0;
+  for (int a0 = beg; a0 < end; a0 += 64 * kBatch) {
+    int ids[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int a = a0 + 64 * u + lane;
+      ids[u] = a < end ? p.idx[a] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (a0 + 64 * u + lane >= end) continue;
+      const int e = ids[u];
+      if (e >= 0 && e < p.E) atomicAdd(&hist[wave * p.E + e], 1);
+      else ++nbad;
+    }
+  }
+  return nbad;
+}
+
+// the slots of chunk g handled by this wave
+__device__ void wave_range(const RouteArgs& p, int g, int* beg, int* end) {
+  const int wave = threadIdx.x >> 6;
+  const int c0 = g * p.chunk, c1 = min(p.A, c0 + p.chunk);
+  const int per = ((c1 - c0 + kRouteWaves - 1) / kRouteWaves + 63) & ~63;
+  *beg = min(c1, c0 + wave * per);
+  *end = min(c1, *beg + per);
+}
+
+// 1. part[g][e] = slots of expert e in chunk g; part[G][g] = out-of-range ids in chunk g
+__global__ __launch_bounds__(kRouteThreads) void route_count_kernel(RouteArgs p) {
+  extern __shared__ int32_t lds[];
+  const int E = p.E, G = gridDim.x, g = blockIdx.x;
+  int32_t* hist = lds;   // [kRouteWaves][E]
+  __shared__ int32_t bad;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) hist[i] = 0;
+  if (tid == 0) bad = 0;
+  __syncthreads();
+  int beg, end;
+  wave_range(p, g, &beg, &end);
+  const int nbad = wave_histogram(p, beg, end, hist);
+  if (nbad) atomicAdd(&bad, nbad);
+  __syncthreads();
+  for (int e = tid; e < E; e += kRouteThreads) {
+    int c = 0;
+    for (int w = 0; w < kRouteWaves; ++w) c += hist[w * E + e];
+    p.part[(int64_t)g * E + e] = c;
+  }
+  if (tid == 0) p.part[(int64_t)G * E + g] = bad;
+}
+
+// 2. offsets, tables (chunk 0) and the stable placement of chunk g
+__global__ __launch_bounds__(kRouteThreads) void route_place_kernel(RouteArgs p) {
+  extern __shared__ int32_t lds[];
+  const int E = p.E, G = gridDim.x, g = blockIdx.x;
+  int32_t* hist = lds;                     // [kRouteWaves][E]: counts, then cursors
+  int32_t* offs = hist + kRouteWaves * E;  // [E]
+  int32_t* tiles = offs + E;               // [E]: counts of e in chunks before g, then M tiles
+  __shared__ int32_t wave_sums[kRouteWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) hist[i] = 0;
+  // expert totals and the counts of earlier chunks, from the count pass
+  for (int e = tid; e < E; e += kRouteThreads) {
+    int tot = 0, before = 0;
+    for (int q = 0; q < G; ++q) {
+      const int c = p.part[(int64_t)q * E + e];
+      tot += c;
+      before += q < g ? c : 0;
+    }
+    offs[e] = tot;
+    tiles[e] = before;
+    if (g == 0 && p.counts) p.counts[e] = tot;
+  }
+  __syncthreads();
+  int beg, end;
+  wave_range(p, g, &beg, &end);
+  (void)wave_histogram(p, beg, end, hist);
+  const int valid = block_exclusive_scan(offs, E, wave_sums);   // (contains a barrier)
+  for (int e = tid; e < E; e += kRouteThreads) {
+    int run = offs[e] + tiles[e];
+    for (int w = 0; w < kRouteWaves; ++w) {
+      const int c = hist[w * E + e];
+      hist[w * E + e] = run;
+      run += c;
+    }
+    if (g == 0) p.offsets[e] = offs[e];
+  }
+  if (g == 0 && tid == 0) {
+    p.offsets[E] = valid;
+    if (p.bad) {
+      int nb = 0;
+      for (int q = 0; q < G; ++q) nb += p.part[(int64_t)G * E + q];
+      *p.bad = nb;
+    }
+  }
+  __syncthreads();
+
+  if (g == 0) {   // M-tile starts for up to two tile heights
+    for (int t = 0; t < 2; ++t) {
+      const int bm = t == 0 ? p.bm0 : p.bm1;
+      int32_t* mt = t == 0 ? p.mt0 : p.mt1;
+      if (bm <= 0 || mt == nullptr) continue;
+      __syncthreads();
+      for (int e = tid; e < E; e += kRouteThreads) {
+        const int c = (e + 1 < E ? offs[e + 1] : valid) - offs[e];
+        tiles[e] = c == 0 ? 0 : (c - 1) / bm + 1;
+      }
+      __syncthreads();
+      const int nt = block_exclusive_scan(tiles, E, wave_sums);
+      for (int e = tid; e < E; e += kRouteThreads) mt[e] = tiles[e];
+      if (tid == 0) mt[E] = nt;
+    }
+    __syncthreads();
+  }
+
+  // stable placement, one 64-slot piece at a time per wave
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int b0 = beg; b0 < end; b0 += 64 * kBatch) {
+    int ids[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int a = b0 + 64 * u + lane;
+      ids[u] = a < end ? p.idx[a] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int a = b0 + 64 * u + lane;
+      const bool in = a < end;
+      const int e = ids[u];
+      const bool ok = in && e >= 0 && e < E;
+      uint64_t same = __ballot(ok);
+      for (int bit = 0; bit < p.id_bits; ++bit) {
+        const bool set = ok && ((e >> bit) & 1);
+        const uint64_t m = __ballot(set);
+        same &= set ? m : ~m;
+      }
+      if (ok) {
+        const int rank = __popcll(same & below);
+        const int pos = hist[wave * E + e] + rank;
+        p.perm[pos] = a;
+        if (p.inv) p.inv[a] = pos;
+        __builtin_amdgcn_wave_barrier();
+        if (rank == 0) hist[wave * E + e] += __popcll(same);
+      } else {
+        __builtin_amdgcn_wave_barrier();
+        if (in && p.inv) p.inv[a] = -1;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+}
+
 }  // namespace
 
 size_t route_lds_bytes(int E) { return sizeof(int32_t) * (size_t)(kRouteWaves * E + 2 * E); }
 
+int route_chunks(int A) {
+  if (A <= kRouteOneBlockMax) return 1;
+  const int chunk = route_chunk(A);
+  return (A + chunk - 1) / chunk;
+}
+
+int route_chunk(int A) {
+  const int want = (A + kRouteMaxChunks - 1) / kRouteMaxChunks;
+  const int c = (want + 63) & ~63;
+  return c < 1024 ? 1024 : c;
+}
+
 hipError_t launch_route(const RouteArgs& args, hipStream_t stream) {
   const size_t lds = route_lds_bytes(args.E);
-  hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), lds, stream, args);
+  const int G = route_chunks(args.A);
+  if (G <= 1 || args.part == nullptr) {
+    hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), lds, stream, args);
+    return hipGetLastError();
+  }
+  RouteArgs a = args;
+  a.chunk = route_chunk(args.A);
+  hipLaunchKernelGGL(route_count_kernel, dim3(G), dim3(kRouteThreads), sizeof(int32_t) * (size_t)kRouteWaves * args.E,
+                     stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(route_place_kernel, dim3(G), dim3(kRouteThreads), lds, stream, a);
   return hipGetLastError();
 }
 

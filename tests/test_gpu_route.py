@@ -37,6 +37,9 @@ def test_route_configs(name):
     (1, 1, 1, "uniform"), (1, 8, 256, "uniform"), (5, 4, 4, "uniform"),   # k == E
     (1000, 1, 1, "uniform"), (777, 3, 1024, "uniform"), (4096, 4, 60, "one"),
     (3000, 8, 256, "few"), (65, 2, 8, "uniform"), (64, 2, 8, "uniform"),
+    # chunked routing (more than 4096 slots): a short last chunk, E = 1024, 64 chunks
+    (1025, 4, 8, "uniform"), (1500, 3, 1024, "uniform"), (70000, 4, 4, "uniform"),
+    (16384, 4, 60, "one"),
 ])
 def test_route_edge_cases(T, k, E, kind):
     rng = np.random.default_rng(T * 31 + k * 7 + E)
@@ -49,13 +52,14 @@ def test_route_edge_cases(T, k, E, kind):
     _check(idx, E)
 
 
-def test_route_out_of_range_ids():
+@pytest.mark.parametrize("T", [200, 3000])   # one workgroup / chunked routing
+def test_route_out_of_range_ids(T):
     rng = np.random.default_rng(5)
-    idx = rng.integers(0, 16, size=(200, 4)).astype(np.int32)
+    idx = rng.integers(0, 16, size=(T, 4)).astype(np.int32)
     bad = np.zeros_like(idx, dtype=bool)
-    bad[3, 1] = bad[50, 0] = bad[199, 3] = True
+    bad[3, 1] = bad[50, 0] = bad[T - 1, 3] = bad[T // 2, 2] = True
     idx_bad = idx.copy()
-    idx_bad[3, 1], idx_bad[50, 0], idx_bad[199, 3] = 16, -1, 1 << 20
+    idx_bad[3, 1], idx_bad[50, 0], idx_bad[T - 1, 3], idx_bad[T // 2, 2] = 16, -1, 1 << 20, -7
     c, o, p, i = _gpu_route(idx_bad, 16)
     # the valid slots are sorted exactly as the oracle sorts them on their own
     flat = idx_bad.reshape(-1)
