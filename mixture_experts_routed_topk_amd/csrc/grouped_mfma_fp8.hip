@@ -417,12 +417,7 @@ hipError_t launch(const GroupedArgs& g, int grid, hipStream_t s) {
 }  // namespace
 
 int grouped_fp8_bm() { return BM; }
-int gateup_fp8_cols() { return Cfg<kOpFp8Wide>::BN / 2; }
 int down_fp8_cols() { return Cfg<kOpFp8>::BN; }
-
-hipError_t launch_gateup_fp8(const GroupedArgs& g, int grid, hipStream_t s) {
-  return launch<kGateUp, kOpFp8Wide>(g, grid, s);
-}
 
 hipError_t launch_down_fp8(const GroupedArgs& g, int grid, hipStream_t s) {
   if (g.slot_out) return launch<kDownSlots, kOpFp8>(g, grid, s);
