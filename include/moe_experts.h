@@ -64,16 +64,21 @@ enum {
    * topk_idx entry was outside [0, E).  Without it such a slot contributes
    * nothing and the call still returns MOE_OK. */
   MOE_FLAG_CHECK_INDICES = 1u,
-  /* Bit-reproducible combine: each slot's weighted expert output is written to
-   * its own row and the k rows of a token are summed in slot order, instead of
-   * floating-point atomic adds (needs the larger workspace). */
+  /* Bit-reproducible combine at every size: each slot's weighted expert output is
+   * written to its own row and the k rows of a token are summed in slot order.
+   * Without the flag this combine is used while the slot rows (4*T*k*H bytes) are at
+   * most 512 MiB, and floating-point atomic adds into a [T, H] accumulator above (or
+   * always with MOE_FLAG_ATOMIC_COMBINE). */
   MOE_FLAG_DETERMINISTIC = 2u,
   /* Path selection (both give the same result within tolerance): the grouped
    * path sorts slots by expert and runs grouped GEMMs; the decode path streams
    * each selected expert's weights once against its few tokens.  Default: decode
    * when T <= 64, grouped otherwise. */
   MOE_FLAG_FORCE_GROUPED = 4u,
-  MOE_FLAG_FORCE_DECODE = 8u
+  MOE_FLAG_FORCE_DECODE = 8u,
+  /* Combine with floating-point atomic adds into a float32 [T, H] accumulator at
+   * every size (the smaller workspace); not with MOE_FLAG_DETERMINISTIC. */
+  MOE_FLAG_ATOMIC_COMBINE = 16u
 };
 
 /* Problem description (plain values; no pointers). */
@@ -102,8 +107,11 @@ int moe_abi_version(void);
 const char* moe_status_str(moe_status s);
 
 /* Bytes of device workspace moe_experts_forward needs for problem *p (host only,
- * closed form, no HIP call).  Grows with T*k*(I + H) and T*H; with
- * MOE_FLAG_DETERMINISTIC it also holds a float32 [T*k, H] buffer. */
+ * closed form, no HIP call).  Grows with T*k*(I + H) and T*H.  When the k rows of a
+ * token are combined as per-slot rows (always with MOE_FLAG_DETERMINISTIC; by default
+ * while 4*T*k*H <= 512 MiB, where that combine is the faster one; never with
+ * MOE_FLAG_ATOMIC_COMBINE) it holds a float32 [T*k, H] buffer instead of the float32
+ * [T, H] accumulator. */
 moe_status moe_workspace_size(const moe_problem* p, size_t* bytes);
 
 /*

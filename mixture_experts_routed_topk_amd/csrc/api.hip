@@ -35,9 +35,10 @@ moe_status validate_problem(const moe_problem* p) {
                          (p->scale_fmt == MOE_SCALE_F32 || p->scale_fmt == MOE_SCALE_UE8M0);
   if (!(combo_f32 || combo_bf16 || combo_fp8)) return MOE_ERR_UNSUPPORTED;
   const uint32_t known = MOE_FLAG_CHECK_INDICES | MOE_FLAG_DETERMINISTIC | MOE_FLAG_FORCE_GROUPED |
-                         MOE_FLAG_FORCE_DECODE;
+                         MOE_FLAG_FORCE_DECODE | MOE_FLAG_ATOMIC_COMBINE;
   if (p->flags & ~known) return MOE_ERR_UNSUPPORTED;
   if ((p->flags & MOE_FLAG_FORCE_GROUPED) && (p->flags & MOE_FLAG_FORCE_DECODE)) return MOE_ERR_UNSUPPORTED;
+  if ((p->flags & MOE_FLAG_DETERMINISTIC) && (p->flags & MOE_FLAG_ATOMIC_COMBINE)) return MOE_ERR_UNSUPPORTED;
   if (p->T < 0 || p->E < 1 || p->E > 1024 || p->k < 1 || p->k > p->E) return MOE_ERR_BAD_SHAPE;
   if (p->H <= 0 || p->I <= 0 || p->H > 65536 || p->I > 65536) return MOE_ERR_BAD_SHAPE;
   if (p->H % 128 != 0) return MOE_ERR_BAD_SHAPE;
@@ -69,6 +70,18 @@ struct Plan {
   int bm;     // row-group height of the tile table the gate/up GEMM walks
   int bm_dn;  // ... and the down GEMM (a second table when it differs)
 };
+
+// Combine by per-slot rows (each slot's weighted row stored, the k rows of a token summed
+// in slot order) rather than float atomics: always with MOE_FLAG_DETERMINISTIC, and by
+// default while the slot rows stay small.  Measured on MI355X: with 134 MB of slot rows
+// (Qwen prefill, T*k = 16384, H = 2048) the down kernel plus the slot sum take 12% less
+// time than the atomic combine; with 1.9 GB (DeepSeek prefill) the atomics win by 3%.
+constexpr int64_t kSlotCombineMaxBytes = int64_t(512) << 20;
+bool slot_combine(const moe_problem& p) {
+  if (p.flags & MOE_FLAG_DETERMINISTIC) return true;
+  if (p.flags & MOE_FLAG_ATOMIC_COMBINE) return false;
+  return 4 * (int64_t)p.T * p.k * p.H <= kSlotCombineMaxBytes;
+}
 
 bool decode_capable(const moe_problem& p) { return p.weight_dtype == MOE_BF16 && p.I % 128 == 0; }
 
@@ -122,7 +135,7 @@ Layout make_layout(const moe_problem& p) {
   L.act_s = fp8 ? take(4 * A * (I / 128)) : o;
   L.x_q = fp8 ? take(T * H) : o;
   L.x_s = fp8 ? take(4 * T * (H / 128)) : o;
-  const bool det = p.flags & MOE_FLAG_DETERMINISTIC;
+  const bool det = slot_combine(p);
   L.acc = det ? o : take(4 * T * H);
   L.slots = det ? take(4 * A * H) : o;
   L.total = o;
@@ -219,7 +232,7 @@ moe_status moe_plan_describe(const moe_problem* p, char* buf, size_t len) {
                                                    : "gateup_mfma32x32x16_on_widened_e4m3_256x128+down_mfma16x16x128_e4m3_256x256";
   snprintf(buf, len, "path=%s weights=%s scales=%s kernels=%s combine=%s workspace_bytes=%zu",
            pl.path == kDecode ? "decode" : "grouped", wname, sname, kern,
-           (p->flags & MOE_FLAG_DETERMINISTIC) ? "slot_rows" : "atomic_f32", L.total);
+           slot_combine(*p) ? "slot_rows" : "atomic_f32", L.total);
   return MOE_OK;
 }
 
@@ -287,7 +300,7 @@ moe_status moe_experts_forward(const moe_problem* p, const void* hidden, const i
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   const int64_t A = p->T * p->k;
-  const bool det = p->flags & MOE_FLAG_DETERMINISTIC;
+  const bool det = slot_combine(*p);   // per-slot rows + slot-order sum (else float atomics)
   const bool f32 = p->weight_dtype == MOE_F32;
 
   int32_t* bad = reinterpret_cast<int32_t*>(ws + L.bad);

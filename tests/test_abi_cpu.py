@@ -72,12 +72,25 @@ def test_problem_validation(kw, status):
         assert n > 0
 
 
-def test_workspace_grows_with_deterministic():
+def test_workspace_by_combine():
+    # per-slot rows [T*k, H] f32 (deterministic, and the default while they are <= 512 MiB)
+    # against the [T, H] f32 accumulator of the atomic combine
     p = P(act=m.BF16, weight=m.BF16, T=4096, H=2048, I=1408, E=60, k=4)
-    _, n0 = _ws(p)
+    _, n_default = _ws(p)
+    p.flags = m.FLAG_ATOMIC_COMBINE
+    _, n_atomic = _ws(p)
     p.flags = m.FLAG_DETERMINISTIC
-    _, n1 = _ws(p)
-    assert n1 - n0 >= 4 * 4096 * 4 * 2048 - 4 * 4096 * 2048
+    _, n_det = _ws(p)
+    assert n_det == n_default
+    assert n_det - n_atomic == 4 * 4096 * 4 * 2048 - 4 * 4096 * 2048
+    # above 512 MiB of slot rows the default is the atomic combine
+    big = P(act=m.BF16, weight=m.BF16, T=8192, H=7168, I=2048, E=256, k=8)
+    _, nb_default = _ws(big)
+    big.flags = m.FLAG_ATOMIC_COMBINE
+    _, nb_atomic = _ws(big)
+    assert nb_default == nb_atomic
+    p.flags = m.FLAG_DETERMINISTIC | m.FLAG_ATOMIC_COMBINE
+    assert _ws(p)[0] == m.ERR_UNSUPPORTED
 
 
 def test_forward_rejects_before_any_hip_call():

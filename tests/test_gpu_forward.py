@@ -17,7 +17,10 @@ from moe_helpers import (assert_close, gpu_out_f64, oracle_out, oracle_weights, 
 
 pytestmark = pytest.mark.gpu
 
-PATHS = {"default": 0, "grouped": m.FLAG_FORCE_GROUPED, "det": m.FLAG_DETERMINISTIC | m.FLAG_FORCE_GROUPED}
+# "grouped": expert-sorted grouped GEMMs with the float-atomic combine; "det": the same
+# with per-slot rows summed in slot order (also the default combine for small layers)
+PATHS = {"default": 0, "grouped": m.FLAG_FORCE_GROUPED | m.FLAG_ATOMIC_COMBINE,
+         "det": m.FLAG_DETERMINISTIC | m.FLAG_FORCE_GROUPED}
 
 
 def _run(D, flags=0):
@@ -61,7 +64,7 @@ def test_small_bf16(path, shape):
 @pytest.mark.parametrize("shape", [dict(T=200, H=128, I=64, E=5, k=2), dict(T=3, H=256, I=128, E=3, k=3)])
 def test_small_fp32(shape):
     spec = synth.Spec("small_fp32", act="f32", weight="f32", renorm=False, seed=3, **shape)
-    _full_check(spec, m.FLAG_FORCE_GROUPED)
+    _full_check(spec, m.FLAG_FORCE_GROUPED | m.FLAG_ATOMIC_COMBINE)
     _full_check(spec, m.FLAG_DETERMINISTIC | m.FLAG_FORCE_GROUPED)
 
 
@@ -70,14 +73,16 @@ def test_all_tokens_one_expert():
     D = device_layer(spec, poison_inactive=False)
     D["idx"].fill_(5)
     D["idx_host"][:] = 5
-    out = gpu_out_f64(_run(D, m.FLAG_FORCE_GROUPED))
     ref = oracle_out(spec, D["x_host"], D["idx_host"], D["w_host"], oracle_weights(spec))
-    assert_close(out, ref, "bf16", "all tokens on one expert")
+    for flags in (m.FLAG_FORCE_GROUPED, m.FLAG_FORCE_GROUPED | m.FLAG_ATOMIC_COMBINE):
+        out = gpu_out_f64(_run(D, flags))
+        assert_close(out, ref, "bf16", f"all tokens on one expert, flags {flags}")
 
 
-def test_qwen_prefill_sampled():
+@pytest.mark.parametrize("flags", [0, m.FLAG_ATOMIC_COMBINE])   # per-slot rows / float atomics
+def test_qwen_prefill_sampled(flags):
     spec = synth.spec_for("qwen_prefill_bf16")
-    _full_check(spec, 0, tokens=sample_tokens(spec.T, 192))
+    _full_check(spec, flags, tokens=sample_tokens(spec.T, 192))
 
 
 def test_qwen_decode_full():
@@ -123,7 +128,8 @@ def test_bad_index_flag():
 
 # ----------------------------------------------------------------------------- decode path
 
-@pytest.mark.parametrize("flags", [0, m.FLAG_FORCE_DECODE, m.FLAG_FORCE_DECODE | m.FLAG_DETERMINISTIC])
+@pytest.mark.parametrize("flags", [0, m.FLAG_FORCE_DECODE, m.FLAG_FORCE_DECODE | m.FLAG_DETERMINISTIC,
+                                   m.FLAG_FORCE_DECODE | m.FLAG_ATOMIC_COMBINE])
 def test_qwen_decode_path(flags):
     spec = synth.spec_for("qwen_decode_bf16")
     D = device_layer(spec)
@@ -159,9 +165,10 @@ def test_decode_matches_grouped_on_tiny_prefill():
     dict(T=200, H=384, I=128, E=64, k=2),     # many empty experts
     dict(T=40, H=128, I=256, E=3, k=3),       # k == E
 ])
-def test_small_fp8(scale, shape):
+@pytest.mark.parametrize("flags", [0, m.FLAG_ATOMIC_COMBINE])
+def test_small_fp8(scale, shape, flags):
     spec = synth.Spec("small_fp8", act="bf16", weight="fp8", scale=scale, renorm=True, seed=5, **shape)
-    _full_check(spec, 0)
+    _full_check(spec, flags)
 
 
 @pytest.mark.parametrize("scale", ["f32", "ue8m0"])
