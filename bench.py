@@ -110,17 +110,21 @@ def layer_totals(spec, active_count):
 
 
 KERNEL_SOURCES = {   # (path, weight dtype, stage) -> kernel source files, for the traffic record
-    ("grouped", "bf16"): ["grouped_bf16.hip"],
-    ("grouped", "fp8"): ["grouped_mfma_fp8.hip"],
-    ("grouped", "f32"): ["grouped_f32.hip"],
-    ("decode", "bf16"): ["decode.hip"],
+    ("grouped", "bf16", "gate_up"): ["grouped_bf16.hip"],
+    ("grouped", "bf16", "down"): ["grouped_bf16.hip"],
+    ("grouped", "fp8", "gate_up"): ["grouped_fp8_gateup.hip"],
+    ("grouped", "fp8", "down"): ["grouped_fp8_down.hip"],
+    ("grouped", "f32", "gate_up"): ["grouped_f32.hip"],
+    ("grouped", "f32", "down"): ["grouped_f32.hip"],
+    ("decode", "bf16", "gate_up"): ["decode.hip"],
+    ("decode", "bf16", "down"): ["decode.hip"],
 }
 
 
-def kernel_digest(path: str, weight: str) -> tuple[str, str]:
+def kernel_digest(path: str, weight: str, stage: str) -> tuple[str, str]:
     """(name, sha256) of the dominant kernel's sources (its file + the shared device headers)."""
     import hashlib
-    files = KERNEL_SOURCES[(path, weight)]
+    files = KERNEL_SOURCES[(path, weight, stage)]
     csrc = os.path.join(ROOT, "mixture_experts_routed_topk_amd", "csrc")
     h = hashlib.sha256()
     for f in files + ["device_common.h", "internal.h"]:
@@ -300,7 +304,7 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": byts / (kavg * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    kname, digest = kernel_digest(plan.split()[0].split("=")[1], spec.weight)
+    kname, digest = kernel_digest(plan.split()[0].split("=")[1], spec.weight, dominant)
     roof["traffic"] = recorded_traffic(kname, dominant, args.config, digest)
     roof.update({"kernel": f"{kname}:{dominant}", "kernel_source_sha256": digest, "avg_ms": kavg, "launches": len(kern_ms),
                  "algorithmic_flops": flops, "algorithmic_bytes": byts,

@@ -229,7 +229,7 @@ moe_status moe_plan_describe(const moe_problem* p, char* buf, size_t len) {
   const char* kern = pl.path == kDecode ? "stream_weights_16tok_mfma16x16x32"
                      : p->weight_dtype == MOE_F32 ? "fma_64x64"
                      : p->weight_dtype == MOE_BF16 ? "mfma32x32x16_bf16_160x256_k64_lds_dma_ring3"
-                                                   : "gateup_mfma32x32x16_on_widened_e4m3_256x128+down_mfma16x16x128_e4m3_256x256";
+                                                   : "gateup_mfma32x32x16_widened_e4m3_160x128_ring4+down_mfma16x16x128_e4m3_128x256_ring3";
   snprintf(buf, len, "path=%s weights=%s scales=%s kernels=%s combine=%s workspace_bytes=%zu",
            pl.path == kDecode ? "decode" : "grouped", wname, sname, kern,
            slot_combine(*p) ? "slot_rows" : "atomic_f32", L.total);

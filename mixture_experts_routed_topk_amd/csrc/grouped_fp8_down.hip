@@ -1,0 +1,294 @@
+// e4m3 down-projection grouped GEMM + routing weight + combine on MFMA (gfx950).
+//
+// The "FP8 and FP4 quantized experts" section of the Experts backends page (and its
+// note): e4m3 weights W_down[e] ([H, I], K = I contiguous) with 128x128 block scales
+// (float32 or UE8M0, used directly) and the e4m3 SwiGLU rows with dynamic per-row
+// scales over 128-column blocks.  Output column n of sorted row m is
+//     y[m, n] = sum over 128-blocks kb of  sa[m, kb] * sw[n, kb] * sum_{k in kb} a[m, k] w[n, k]
+// The inner sum of one block is one 16x16x128 e4m3 MFMA; its result is folded into the
+// float32 accumulator times the two scales.  The epilogue multiplies by the routing
+// weight and adds the row into the token's float32 output row (hardware float atomics)
+// or stores it to the slot's own row (per-slot combine).
+//
+// Tiles of up to 128 rows x 256 output columns; eight waves in a 2 x 4 grid, wave
+// (wm, wn) owning the 16-row fragments wm, wm + 2, .., wm + 6 and output columns
+// 64 wn .. 64 wn + 63 (four 16-column fragments).  K advances in slices of 128 codes (one
+// scale block) held in a three-slot LDS ring filled by global->LDS DMA: slices kt + 1
+// and kt + 2 stream in while slice kt is multiplied, the DMA of kt + 2 spread over the
+// slice's work.  Slot rows are 128 bytes with 16-byte chunks XOR-permuted by
+// (row >> 1) & 7; the row scales of the slice ride in the slot.  Work items (expert,
+// N tile, M tile), M fastest, an expert's rows split evenly over its M tiles (multiples
+// of 32 rows, at most 128); persistent grid with XCD-contiguous runs of items.
+#include <type_traits>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 512;
+constexpr int NW = 8;
+constexpr int BM = 128;                    // tile rows (eight 16-row fragments)
+constexpr int BN = 256;                    // output columns (weight rows)
+constexpr int MFRAG = 4;                   // 16-row fragments per wave (2 i + wm)
+constexpr int NFRAG = 4;                   // 16-column fragments per wave
+constexpr int ROWB = 128;                  // bytes (= codes = K) of a tile row per slice
+constexpr int NSTAGE = 3;
+constexpr int SA_OFF = (BM + BN) * ROWB;   // per slot: A rows, B rows, then the row scales
+constexpr int SA_N = 128;                  // row-scale entries per slot (two DMAs of 64)
+constexpr int STAGE = SA_OFF + 4 * SA_N;   // 49664 bytes
+constexpr int RPI = 1024 / ROWB;           // tile rows per DMA instruction
+constexpr int ALD = BM / RPI / NW;         // A DMA instructions per wave per slice (2)
+constexpr int BLD = BN / RPI / NW;         // B DMA instructions per wave per slice (4)
+constexpr int kMaxE = 1024;
+constexpr int kMaxKB = 512;                // K / 128 (K = I <= 65536)
+static_assert(ALD <= 4 && BLD == 4, "the DMA of a slice is spread over four parts");
+
+enum { kDownAtomic = 1, kDownSlots = 2 };
+
+__device__ __forceinline__ int chunk_slot(int row, int c) { return c ^ ((row >> 1) & 7); }
+
+__device__ __forceinline__ float ue8m0_value(uint32_t b) {
+  if (b == 0) return __uint_as_float(0x00400000u);   // 2^-127
+  if (b == 255) return __uint_as_float(0x7fc00000u);
+  return __uint_as_float(b << 23);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kThreads, 1) void grouped_fp8_down_kernel(GroupedArgs g) {
+  __shared__ __attribute__((aligned(1024))) char ring[NSTAGE][STAGE];
+  __shared__ float sSb[2][kMaxKB];          // the item's weight block scales (two row blocks)
+  __shared__ uint16_t sMt[kMaxE + 1];
+  __shared__ int sTok[BM];
+  __shared__ float sWt[BM];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int gx = gridDim.x >> 3;
+  const int xcd = blockIdx.x & 7, xslot = blockIdx.x >> 3;
+  const int E = g.E;
+  const int KT = g.K / ROWB;
+  const char* __restrict__ Abase = static_cast<const char*>(g.a);
+  const char* __restrict__ Sbase = reinterpret_cast<const char*>(g.a_scale);
+  const uint32_t a_row_bytes = (uint32_t)g.lda;
+  const uint32_t b_row_bytes = (uint32_t)g.K;
+
+  const int n_mt = g.mt[E];
+  const bool mt_lds = n_mt < 65536;
+  if (mt_lds)
+    for (int i = tid; i <= E; i += kThreads) sMt[i] = (uint16_t)g.mt[i];
+  __syncthreads();
+  const int n_items = n_mt * g.NT;
+  auto mt_at = [&](int i) __attribute__((always_inline)) -> int { return mt_lds ? (int)sMt[i] : g.mt[i]; };
+
+  const int ld_row = lane >> 3, ld_slot = lane & 7;
+  const uint32_t ring0 = lds_addr(&ring[0][0]);
+  // 16x16x128 operands: lane holds row (lane & 15) and codes 32 g4 .. 32 g4 + 31 of the
+  // slice: logical chunks 2 g4 and 2 g4 + 1
+  const uint32_t foff0 = (uint32_t)(l16 * ROWB + (chunk_slot(l16, 2 * g4) << 4));
+  const uint32_t foff1 = (uint32_t)(l16 * ROWB + (chunk_slot(l16, 2 * g4 + 1) << 4));
+
+  f32x4 acc[MFRAG][NFRAG];
+
+  for (int w = xcd * gx + xslot; w < n_items; w += gridDim.x) {
+    int e;
+    {
+      int lo = 0, hi = E - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (mt_at(mid) * g.NT <= w) lo = mid; else hi = mid - 1;
+      }
+      e = lo;
+    }
+    const int mt0 = mt_at(e);
+    const int mt_e = mt_at(e + 1) - mt0;
+    const int local = w - mt0 * g.NT;
+    const int nt = local / mt_e;
+    const int mloc = local - nt * mt_e;
+    const int off0 = g.offsets[e], off1 = g.offsets[e + 1];
+    const int cnt = off1 - off0;
+    const int per = min(BM, ((cnt + mt_e - 1) / mt_e + 31) & ~31);
+    const int row0 = off0 + mloc * per;
+    const int rows = min(per, off1 - row0);
+    if (rows <= 0) continue;
+    const char* __restrict__ Bexp = static_cast<const char*>(g.b) + (int64_t)e * g.b_expert_stride;
+
+    auto b_row = [&](int c) __attribute__((always_inline)) -> int { return min(nt * BN + c, g.H - 1); };
+    auto a_src = [&](int r) __attribute__((always_inline)) -> int { return row0 + min(r, rows - 1); };
+
+    // the item's weight block scales: row blocks of output columns nt*256 .. +127, +128 .. +255
+    {
+      const int KB = KT;
+      const int64_t nblk_rows = g.b_rows / 128;
+      for (int i = tid; i < 2 * KB; i += kThreads) {
+        const int hb = i < KB ? 0 : 1;
+        const int kb = i - hb * KB;
+        const int64_t blk = (int64_t)e * nblk_rows + min(nt * BN + 128 * hb, g.H - 1) / 128;
+        float v;
+        if (g.b_scale_ue8m0) v = ue8m0_value(static_cast<const uint8_t*>(g.b_scale)[blk * KB + kb]);
+        else v = static_cast<const float*>(g.b_scale)[blk * KB + kb];
+        sSb[hb][kb] = v;
+      }
+    }
+    int my_tok = 0;
+    float my_wt = 0.f;
+    if (tid < rows) {
+      const int slot = g.perm[row0 + tid];
+      my_tok = MODE == kDownAtomic ? slot / g.k : slot;
+      my_wt = g.topk_w[slot];
+    }
+
+    const int nfr16 = (rows + 15) / 16;
+    const int nblk = nfr16 * (16 / RPI);   // A blocks covering the 16-row fragments with rows
+    uint32_t aoff[ALD], boff[BLD];
+#pragma unroll
+    for (int q = 0; q < ALD; ++q) {
+      const int r = RPI * (wave + NW * q) + ld_row;
+      aoff[q] = (uint32_t)a_src(r) * a_row_bytes + (uint32_t)(chunk_slot(r, ld_slot) << 4);
+    }
+#pragma unroll
+    for (int q = 0; q < BLD; ++q) {
+      const int c = RPI * (wave + NW * q) + ld_row;
+      boff[q] = (uint32_t)b_row(c) * b_row_bytes + (uint32_t)(chunk_slot(c, ld_slot) << 4);
+    }
+    const bool sa_wave = wave < SA_N / 64;
+    const uint32_t soff = (uint32_t)a_src(64 * (wave & 1) + lane) * (uint32_t)(KT * 4);
+
+    auto issue_part = [&](int kt, int slot, int p) __attribute__((always_inline)) {
+      const uint32_t st = ring0 + (uint32_t)(slot * STAGE);
+      if (p < ALD && wave + NW * p < nblk)
+        dma_lds_x4(Abase + (int64_t)kt * ROWB, aoff[p < ALD ? p : 0], st + (uint32_t)((wave + NW * p) * 1024));
+      dma_lds_x4(Bexp + (int64_t)kt * ROWB, boff[p], st + (uint32_t)(BM * ROWB + (wave + NW * p) * 1024));
+      if (p == 3 && sa_wave) dma_lds_x1(Sbase + (int64_t)kt * 4, soff, st + (uint32_t)(SA_OFF + wave * 256));
+    };
+    auto issue = [&](int kt, int slot) __attribute__((always_inline)) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) issue_part(kt, slot, p);
+    };
+    int na = 0;
+#pragma unroll
+    for (int q = 0; q < ALD; ++q) na += wave + NW * q < nblk ? 1 : 0;
+    const int nld = __builtin_amdgcn_readfirstlane(na + BLD + (sa_wave ? 1 : 0));   // 4..7
+    auto wait_one_slice = [&]() __attribute__((always_inline)) {
+      switch (nld) {
+        case 4: wait_vmcnt<4>(); break;
+        case 5: wait_vmcnt<5>(); break;
+        case 6: wait_vmcnt<6>(); break;
+        default: wait_vmcnt<7>(); break;
+      }
+    };
+
+#pragma unroll
+    for (int i = 0; i < MFRAG; ++i)
+#pragma unroll
+      for (int j = 0; j < NFRAG; ++j) acc[i][j] = f32x4{};
+
+    // multiply slice kt (slot `slot`); with `next`, slice kt + 2 is issued into `nslot`,
+    // one part per 16-row fragment step
+    auto compute = [&](auto NI_, int kt, int slot, bool next, int nslot) __attribute__((always_inline)) {
+      constexpr int NI = decltype(NI_)::value;
+      const char* As = &ring[slot][0];
+      const char* Bs = As + BM * ROWB;
+      const float* Sa = reinterpret_cast<const float*>(As + SA_OFF);
+      const float sb = sSb[wn >> 1][kt];   // the wave's 64 columns lie in one 128-row block
+      i32x8 bf[NFRAG];
+#pragma unroll
+      for (int j = 0; j < NFRAG; ++j) {
+        const char* bp = Bs + (wn * 64 + j * 16) * ROWB;
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(bp + foff0);
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(bp + foff1);
+        bf[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i < NI) {
+          const char* ap = As + (2 * i + wm) * 16 * ROWB;
+          const i32x4 lo = *reinterpret_cast<const i32x4*>(ap + foff0);
+          const i32x4 hi = *reinterpret_cast<const i32x4*>(ap + foff1);
+          const i32x8 af = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          const f32x4 sa = *reinterpret_cast<const f32x4*>(&Sa[(2 * i + wm) * 16 + 4 * g4]);
+          f32x4 s;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) s[q] = sa[q] * sb;
+#pragma unroll
+          for (int j = 0; j < NFRAG; ++j) {
+            const f32x4 pr = mfma_16x16x128_e4m3(af, bf[j], f32x4{});
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[i][j][q] = fmaf(pr[q], s[q], acc[i][j][q]);
+          }
+        }
+        if (next) issue_part(kt + 2, nslot, i);
+      }
+    };
+    auto kloop = [&](auto NI_) __attribute__((always_inline)) {
+      issue(0, 0);
+      if (1 < KT) issue(1, 1);
+      int slot = 0;
+      for (int kt = 0; kt < KT; ++kt) {
+        if (kt + 1 < KT) wait_one_slice();
+        else wait_vmcnt<0>();
+        __syncthreads();
+        const int nslot = slot == 0 ? 2 : slot - 1;
+        compute(NI_, kt, slot, kt + 2 < KT, nslot);
+        slot = slot == 2 ? 0 : slot + 1;
+      }
+    };
+    __syncthreads();   // sSb of this item is visible
+    switch ((nfr16 - wm + 1) / 2) {
+      case 4: kloop(std::integral_constant<int, 4>{}); break;
+      case 3: kloop(std::integral_constant<int, 3>{}); break;
+      case 2: kloop(std::integral_constant<int, 2>{}); break;
+      case 1: kloop(std::integral_constant<int, 1>{}); break;
+      default: kloop(std::integral_constant<int, 0>{}); break;
+    }
+
+    if (tid < BM) {
+      sTok[tid] = my_tok;
+      sWt[tid] = my_wt;
+    }
+    __syncthreads();
+    // 16x16 fragment (i, j): element q at tile row (2 i + wm) * 16 + 4 g4 + q, column
+    // 64 wn + 16 j + l16
+#pragma unroll
+    for (int i = 0; i < MFRAG; ++i) {
+      if ((2 * i + wm) * 16 >= rows) break;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = (2 * i + wm) * 16 + 4 * g4 + q;
+        if (r >= rows) continue;
+        const float wt = sWt[r];
+        const int64_t tok = sTok[r];
+#pragma unroll
+        for (int j = 0; j < NFRAG; ++j) {
+          const int col = nt * BN + wn * 64 + j * 16 + l16;
+          if (col < g.H) {
+            if (MODE == kDownAtomic) unsafeAtomicAdd(g.acc_out + tok * g.H + col, wt * acc[i][j][q]);
+            else g.slot_out[tok * g.H + col] = wt * acc[i][j][q];
+          }
+        }
+      }
+    }
+    __syncthreads();   // ring, sSb, sTok / sWt are reused by the next item
+  }
+}
+
+template <int MODE>
+hipError_t launch(const GroupedArgs& g, int grid, hipStream_t s) {
+  if (g.K / ROWB > kMaxKB) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((grouped_fp8_down_kernel<MODE>), dim3(grid), dim3(kThreads), 0, s, g);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int grouped_fp8_bm() { return BM; }
+int down_fp8_cols() { return BN; }
+
+hipError_t launch_down_fp8(const GroupedArgs& g, int grid, hipStream_t s) {
+  return g.slot_out ? launch<kDownSlots>(g, grid, s) : launch<kDownAtomic>(g, grid, s);
+}
+
+}  // namespace moe
