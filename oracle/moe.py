@@ -93,6 +93,37 @@ def route(topk_idx: np.ndarray, E: int):
     return as32(counts), as32(offsets), as32(perm), as32(inv)
 
 
+def router_topk(logits: np.ndarray, k: int, renorm: bool):
+    """The router step in front of the bookkeeping (softmax -> top-k -> optional renorm).
+
+    logits [T, E] are taken exactly in fp64.  For each token:
+      p[e]   = exp(logit[e] - max) / sum_e' exp(logit[e'] - max)   (softmax over all E);
+      chosen = the k experts of largest p, taken one at a time, equal p going to the
+               lower expert id;
+      w[j]   = p[chosen[j]], divided by the sum over the k chosen when renorm.
+    Returns (idx int32 [T, k], w fp64 [T, k]), idx in the order chosen.
+    """
+    lg = np.asarray(logits, dtype=np.float64)
+    T, E = lg.shape
+    if not 1 <= k <= E:
+        raise ValueError(f"k = {k} outside [1, {E}]")
+    idx = np.zeros((T, k), dtype=np.int32)
+    w = np.zeros((T, k), dtype=np.float64)
+    for t in range(T):
+        row = lg[t]
+        ex = np.exp(row - row.max())
+        p = ex / ex.sum()
+        left = p.copy()
+        for j in range(k):
+            e = int(np.argmax(left))     # first of the largest: ties to the lower id
+            idx[t, j] = e
+            w[t, j] = p[e]
+            left[e] = -np.inf
+        if renorm:
+            w[t] /= w[t].sum()
+    return idx, w
+
+
 # ----------------------------------------------------------------------------- fp8 rows
 
 def quant_rows(v: np.ndarray):
