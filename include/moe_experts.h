@@ -164,6 +164,29 @@ moe_status moe_route(const moe_problem* p, const int32_t* topk_idx, int32_t* cou
                      size_t workspace_bytes, void* stream);
 
 /*
+ * The router step in front of the routing bookkeeping (Experts backends page,
+ * introduction: tokens go to the top-k experts the router scores, and their
+ * outputs are combined with the routing weights).  For each token t:
+ *   p[e]        = softmax over the E logits of row t (float32: max-shifted expf,
+ *                 divided by the sum);
+ *   topk_idx[t] = the k experts of largest p in decreasing order, equal logits
+ *                 going to the lower expert id (softmax is increasing, so the
+ *                 choice is made on the logits themselves, exactly);
+ *   topk_w[t]   = their p, divided by the sum of the k when renorm != 0;
+ * then the bookkeeping of moe_route on the chosen ids, in the same pass.
+ *
+ *   logits   [T, E] float32, device; every row needs a finite entry and no NaN
+ *   topk_idx [T, k] int32 out;  topk_w [T, k] float32 out
+ *   counts, offsets, perm, inv: as moe_route
+ *
+ * k <= 64 (MOE_ERR_UNSUPPORTED above).  Same workspace rules as moe_route;
+ * ids are always in range, so no index check is needed.
+ */
+moe_status moe_route_logits(const moe_problem* p, const float* logits, int renorm, int32_t* topk_idx,
+                            float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                            int32_t* inv, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Dynamic per-row e4m3 quantisation (page section "FP8 and FP4 quantized
  * experts": per-row activation scales, static per-tensor scales rejected).
  * For each row and each group of 128 consecutive columns:

@@ -16,7 +16,7 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "experts_forward", "route", "quantize_rows_fp8", "workspace_size", "plan_describe",
+    "experts_forward", "route", "route_logits", "quantize_rows_fp8", "workspace_size", "plan_describe",
     "Problem", "MoeError", "lib", "FLAG_CHECK_INDICES", "FLAG_DETERMINISTIC", "FLAG_ATOMIC_COMBINE",
     "FLAG_FORCE_GROUPED", "FLAG_FORCE_DECODE", "LIB_PATH",
 ]
@@ -37,7 +37,8 @@ FLAG_FORCE_DECODE = 8
 FLAG_ATOMIC_COMBINE = 16
 
 EXPORTS = ["moe_abi_version", "moe_status_str", "moe_workspace_size", "moe_experts_forward",
-           "moe_route", "moe_quantize_rows_fp8", "moe_plan_describe", "moe_set_stage_events"]
+           "moe_route", "moe_route_logits", "moe_quantize_rows_fp8", "moe_plan_describe",
+           "moe_set_stage_events"]
 
 # stage ids (moe_set_stage_events)
 STAGES = ["zero", "route", "quant_x", "gate_up", "quant_act", "down", "finalize"]
@@ -80,6 +81,8 @@ def lib():
     L.moe_experts_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_route.restype = ctypes.c_int
     L.moe_route.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_route_logits.restype = ctypes.c_int
+    L.moe_route_logits.argtypes = [P, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_quantize_rows_fp8.restype = ctypes.c_int
     L.moe_quantize_rows_fp8.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, vp, vp, vp]
     L.moe_plan_describe.restype = ctypes.c_int
@@ -216,6 +219,29 @@ def route(topk_idx: torch.Tensor, E: int, flags: int = 0, workspace=None):
     _check(lib().moe_route(ctypes.byref(prob), _ptr(topk_idx), _ptr(counts), _ptr(offsets),
                            _ptr(perm), _ptr(inv), _ptr(workspace), workspace.numel(), _stream(dev)))
     return counts, offsets, perm[: T * k], inv[: T * k]
+
+
+def route_logits(logits: torch.Tensor, k: int, renorm: bool = False, workspace=None):
+    """Router + bookkeeping from float32 logits [T, E]: (topk_idx[T,k] int32, topk_w[T,k] float32,
+    counts[E], offsets[E+1], perm[T*k], inv[T*k]); see moe_route_logits."""
+    _need_gpu("logits", logits)
+    if logits.dtype != torch.float32 or logits.dim() != 2 or not logits.is_contiguous():
+        raise ValueError("logits must be a contiguous 2-D float32 tensor")
+    T, E = logits.shape
+    dev = logits.device
+    prob = Problem(T, 128, 128, E, k, BF16, BF16, SCALE_NONE, 0)
+    idx = torch.empty((max(T, 1), k), dtype=torch.int32, device=dev)
+    w = torch.empty((max(T, 1), k), dtype=torch.float32, device=dev)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(max(T * k, 1), dtype=torch.int32, device=dev)
+    inv = torch.empty(max(T * k, 1), dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(workspace_size(prob), dtype=torch.uint8, device=dev)
+    _check(lib().moe_route_logits(ctypes.byref(prob), _ptr(logits), int(bool(renorm)), _ptr(idx), _ptr(w),
+                                  _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(inv), _ptr(workspace),
+                                  workspace.numel(), _stream(dev)))
+    return idx[:T], w[:T], counts, offsets, perm[: T * k], inv[: T * k]
 
 
 def set_stage_events(handles):

@@ -273,6 +273,44 @@ moe_status moe_route(const moe_problem* p, const int32_t* topk_idx, int32_t* cou
   return MOE_OK;
 }
 
+moe_status moe_route_logits(const moe_problem* p, const float* logits, int renorm, int32_t* topk_idx,
+                            float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                            int32_t* inv, void* workspace, size_t workspace_bytes, void* stream) {
+  moe_status st = validate_problem(p);
+  if (st != MOE_OK) return st;
+  if (p->k > 64) return MOE_ERR_UNSUPPORTED;
+  if (!counts || !offsets || !workspace) return MOE_ERR_NULL_ARG;
+  if (p->T > 0 && (!logits || !topk_idx || !topk_w || !perm || !inv)) return MOE_ERR_NULL_ARG;
+  if (!aligned4(logits) || !aligned4(topk_idx) || !aligned4(topk_w) || !aligned4(counts) || !aligned4(offsets) ||
+      !aligned4(perm) || !aligned4(inv) || !aligned16(workspace))
+    return MOE_ERR_BAD_SHAPE;
+  const Layout L = make_layout(*p);
+  if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  DeviceRecord* dev = nullptr;
+  if ((st = device_record(&dev)) != MOE_OK) return st;
+  (void)hipGetLastError();  // see moe_experts_forward
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  RouteArgs r{};
+  r.idx = topk_idx;
+  r.A = (int)(p->T * p->k);
+  r.E = p->E;
+  r.id_bits = id_bits(p->E);
+  r.counts = counts;
+  r.offsets = offsets;
+  r.perm = perm;
+  r.inv = inv;
+  r.bad = reinterpret_cast<int32_t*>(ws + L.bad);
+  r.part = reinterpret_cast<int32_t*>(ws + L.route_part);
+  r.logits = logits;
+  r.k = p->k;
+  r.renorm = renorm != 0;
+  r.idx_out = topk_idx;
+  r.w_out = topk_w;
+  MOE_HIP_CHECK(launch_route(r, s));   // (T = 0: zero counts and offsets only)
+  return MOE_OK;
+}
+
 moe_status moe_experts_forward(const moe_problem* p, const void* hidden, const int32_t* topk_idx, const float* topk_w,
                                const void* w_gate_up, const void* w_down, const void* w_gate_up_scale,
                                const void* w_down_scale, void* out, void* workspace, size_t workspace_bytes,

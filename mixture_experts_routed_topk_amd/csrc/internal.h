@@ -9,7 +9,7 @@ namespace moe {
 
 // ---------------------------------------------------------------------------- routing
 struct RouteArgs {
-  const int32_t* idx;  // [A] flattened topk_idx
+  const int32_t* idx;  // [A] flattened topk_idx (with logits: the router's output, idx_out)
   int A;
   int E;
   int id_bits;         // bits needed for ids in [0, E)
@@ -27,6 +27,12 @@ struct RouteArgs {
   // null, one workgroup routes the whole batch)
   int32_t* part;
   int chunk;           // (set by launch_route)
+  // optional router step in front: logits [T][E] float32 -> idx_out [T][k], w_out [T][k]
+  const float* logits;
+  int k;
+  int renorm;          // divide the k weights by their sum
+  int32_t* idx_out;
+  float* w_out;
 };
 constexpr int kRouteOneBlockMax = 4096;
 constexpr int kRouteMaxChunks = 64;

@@ -28,6 +28,72 @@ constexpr int kRouteThreads = 512;
 constexpr int kRouteWaves = kRouteThreads / kWave;
 constexpr int kBatch = 8;             // 64-slot pieces whose ids are loaded together
 
+// ---------------------------------------------------------------------------- router
+// The router of token t, on one wave: softmax over its E logits, the k experts of largest
+// probability taken one at a time (softmax is increasing, so by logit; equal logits go
+// to the lower id), their probabilities, divided by their sum with renorm.  Lane l holds
+// logits l, l + 64, ... (E <= 1024); lane j < k keeps the j-th choice.
+__device__ void route_token(const RouteArgs& p, int t) {
+  constexpr int J = 16;
+  const int lane = threadIdx.x & 63;
+  const int E = p.E, k = p.k;
+  const float* row = p.logits + (int64_t)t * E;
+  float v[J];
+  float m = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int e = lane + 64 * j;
+    v[j] = e < E ? row[e] : -INFINITY;
+    m = fmaxf(m, v[j]);
+  }
+  for (int d = 32; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+    if (lane + 64 * j < E) s += expf(v[j] - m);
+  for (int d = 32; d >= 1; d >>= 1) s += __shfl_xor(s, d, 64);
+  uint32_t taken = 0;   // bit j: logit j of this lane already chosen
+  int my_id = 0;
+  float my_w = 0.f, wsum = 0.f;
+  for (int r = 0; r < k; ++r) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {   // this lane's best remaining (ids ascend with j)
+      const int e = lane + 64 * j;
+      if (e < E && !((taken >> j) & 1u) && (bi == 0x7fffffff || v[j] > bv)) {
+        bv = v[j];
+        bi = e;
+      }
+    }
+    for (int d = 32; d >= 1; d >>= 1) {   // larger logit, then lower id
+      const float ov = __shfl_xor(bv, d, 64);
+      const int oi = __shfl_xor(bi, d, 64);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    const float pr = expf(bv - m) / s;
+    if (lane == r) {
+      my_id = bi;
+      my_w = pr;
+    }
+    wsum += pr;
+  }
+  if (lane < k) {
+    p.idx_out[(int64_t)t * k + lane] = my_id;
+    p.w_out[(int64_t)t * k + lane] = p.renorm ? my_w / wsum : my_w;
+  }
+}
+
+// the router alone, one wave per token (in front of the chunked bookkeeping)
+__global__ __launch_bounds__(kRouteThreads) void router_kernel(RouteArgs p) {
+  const int t = blockIdx.x * kRouteWaves + (threadIdx.x >> 6);
+  if (t < p.A / p.k) route_token(p, t);
+}
+
 // Exclusive scan over v[0..n) in LDS (n <= 2 * kRouteThreads); returns the total.
 __device__ int block_exclusive_scan(int32_t* v, int n, int32_t* wave_sums) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -68,6 +134,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs p) {
 
   for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) hist[i] = 0;
   if (tid == 0) bad = 0;
+  if (p.logits) {   // the router step first: every token's k choices into idx_out
+    for (int t = wave; t < A / p.k; t += kRouteWaves) route_token(p, t);
+  }
   __syncthreads();
 
   // contiguous slot range of this wave, in whole 64-slot pieces
@@ -356,6 +425,12 @@ hipError_t launch_route(const RouteArgs& args, hipStream_t stream) {
   }
   RouteArgs a = args;
   a.chunk = route_chunk(args.A);
+  if (args.logits) {
+    const int T = args.A / args.k;
+    hipLaunchKernelGGL(router_kernel, dim3((T + kRouteWaves - 1) / kRouteWaves), dim3(kRouteThreads), 0, stream, a);
+    const hipError_t e0 = hipGetLastError();
+    if (e0 != hipSuccess) return e0;
+  }
   hipLaunchKernelGGL(route_count_kernel, dim3(G), dim3(kRouteThreads), sizeof(int32_t) * (size_t)kRouteWaves * args.E,
                      stream, a);
   hipError_t e = hipGetLastError();

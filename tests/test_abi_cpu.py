@@ -148,3 +148,16 @@ def test_python_wrapper_rejects_cpu_tensors():
     with pytest.raises(ValueError):
         m.experts_forward(x, torch.zeros(4, 2, dtype=torch.int32), torch.zeros(4, 2),
                           torch.zeros(8, 512, 128), torch.zeros(8, 128, 256))
+
+
+def test_route_logits_rejects_before_any_hip_call():
+    L = m.lib()
+    fake = ctypes.c_void_p(0x10000)  # never dereferenced: validation fails first
+    p = P(act=m.BF16, weight=m.BF16, T=4, H=128, I=128, E=100, k=65)
+    st = L.moe_route_logits(ctypes.byref(p), fake, 0, fake, fake, fake, fake, fake, fake, fake, 1 << 40, None)
+    assert st == m.ERR_UNSUPPORTED      # k > 64
+    p.k = 4
+    st = L.moe_route_logits(ctypes.byref(p), None, 0, fake, fake, fake, fake, fake, fake, fake, 1 << 40, None)
+    assert st == m.ERR_NULL_ARG         # no logits
+    st = L.moe_route_logits(ctypes.byref(p), fake, 0, fake, fake, fake, fake, fake, fake, fake, 16, None)
+    assert st == m.ERR_WORKSPACE
