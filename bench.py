@@ -71,6 +71,46 @@ class HipEvents:
             self.hip.hipEventDestroy(ctypes.c_void_p(e))
 
 
+def router_step(spec, dev, iters=50):
+    """The router step + bookkeeping (moe_route_logits) on seeded float32 logits of this layer's
+    [T, E] shape: GPU time per call, from two events around `iters` back-to-back calls on
+    torch's stream (which the library uses) with every buffer allocated beforehand, and the
+    bytes it must move."""
+    import ctypes as C
+    import torch
+    import mixture_experts_routed_topk_amd as m
+    g = torch.Generator().manual_seed(0)
+    T, E, k = spec.T, spec.E, spec.k
+    lg = torch.randn((T, E), generator=g, dtype=torch.float32).to(dev)
+    prob = m.Problem(T, 128, 128, E, k, m.BF16, m.BF16, m.SCALE_NONE, 0)
+    ws = torch.empty(m.workspace_size(prob), dtype=torch.uint8, device=dev)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    cnt = torch.empty(E, dtype=torch.int32, device=dev)
+    off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(T * k, dtype=torch.int32, device=dev)
+    inv = torch.empty(T * k, dtype=torch.int32, device=dev)
+    stream = C.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    args = [C.byref(prob), C.c_void_p(lg.data_ptr()), int(spec.renorm)] + \
+        [C.c_void_p(t.data_ptr()) for t in (idx, w, cnt, off, perm, inv, ws)] + [ws.numel(), stream]
+    call = m.lib().moe_route_logits
+    for _ in range(3):
+        if call(*args) != 0:
+            raise RuntimeError("moe_route_logits failed")
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(iters):
+        call(*args)
+    b.record()
+    b.synchronize()
+    ms = a.elapsed_time(b) / iters
+    byts = T * E * 4 + T * k * 8 + spec.A * 8 + E * 8
+    return {"what": "router (softmax, top-k, renorm) + routing bookkeeping from float32 logits",
+            "ms": ms, "calls": iters, "bytes": byts, "GB/s": byts / (ms * 1e-3) / 1e9,
+            "bound": "launch latency (a few MB at most)"}
+
+
 def algorithmic(spec, active_count, stage):
     """(flops, bytes) the method must do/move in one launch of a stage."""
     A, H, I = spec.A, spec.H, spec.I
@@ -335,6 +375,7 @@ def main():
         "stages_ms": stage_ms,
         "roofline": roof,
     }
+    res["router_step"] = router_step(spec, dev)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(spec, D, args.cpu_seconds)
     print(json.dumps(res), flush=True)
