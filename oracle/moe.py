@@ -57,6 +57,23 @@ def silu(z: np.ndarray) -> np.ndarray:
         return z / (1.0 + np.exp(-z))
 
 
+def gelu(z: np.ndarray) -> np.ndarray:
+    """z * Phi(z) = z / 2 * erfc(-z / sqrt(2)) in fp64: the exact (erf) form of GELU, the
+    gate of GeGLU (SonicMoE section: gated activations silu, gelu or relu map to SwiGLU,
+    GeGLU or ReGLU).  erfc keeps the far negative tail accurate (1 + erf would cancel)."""
+    from scipy.special import erfc
+    z = np.asarray(z, dtype=np.float64)
+    return 0.5 * z * erfc(-z / np.sqrt(2.0))
+
+
+def relu(z: np.ndarray) -> np.ndarray:
+    """max(z, 0), the gate of ReGLU."""
+    return np.maximum(np.asarray(z, dtype=np.float64), 0.0)
+
+
+GATES = {"silu": silu, "gelu": gelu, "relu": relu}
+
+
 # ----------------------------------------------------------------------------- routing
 
 def route(topk_idx: np.ndarray, E: int):
@@ -220,9 +237,10 @@ def _prepare_x(x: np.ndarray, act: str, fp8: bool) -> np.ndarray:
     return xf
 
 
-def _swiglu_then_requant(gu: np.ndarray, I: int, fp8: bool) -> np.ndarray:
-    """gu [..., 2I] fp64 -> the activation fed to the down projection."""
-    a = silu(gu[..., :I]) * gu[..., I:]
+def _swiglu_then_requant(gu: np.ndarray, I: int, fp8: bool, gate: str = "silu") -> np.ndarray:
+    """gu [..., 2I] fp64 -> the activation fed to the down projection: gate(g) * u with the
+    gate function silu (SwiGLU, the default), gelu (GeGLU) or relu (ReGLU)."""
+    a = GATES[gate](gu[..., :I]) * gu[..., I:]
     if fp8:
         a2 = np.atleast_2d(f64_to_f32(a))
         q, s = quant_rows(a2)
@@ -241,12 +259,14 @@ def out_as_f64(out: np.ndarray, act: str) -> np.ndarray:
 
 def forward(x: np.ndarray, idx: np.ndarray, w: np.ndarray, weights: ExpertWeights, *,
             act: str, E: Optional[int] = None, mode: str = "fast",
-            tokens: Optional[Sequence[int]] = None):
+            tokens: Optional[Sequence[int]] = None, gate: str = "silu"):
     """Routed top-k experts forward.
 
     x: [T, H] (fp32 values or bf16 bits); idx: int [T, k]; w: float32 [T, k].
     E: number of experts (taken from the weight arrays when they are arrays).
     tokens: optional subset of token rows to evaluate (each token is independent).
+    gate: the gated activation, "silu" (SwiGLU), "gelu" (GeGLU, exact erf form) or "relu"
+    (ReGLU).
     Returns (acc fp64 [n, H], out [n, H] in the output storage) for the chosen
     rows (all T rows when tokens is None), in the order of `tokens`.
     """
@@ -274,7 +294,7 @@ def forward(x: np.ndarray, idx: np.ndarray, w: np.ndarray, weights: ExpertWeight
                     cache[e] = (weights.gate_up_f64(e), weights.down_f64(e))
                 wgu, wd = cache[e]
                 I = wd.shape[1]
-                a = _swiglu_then_requant(wgu @ xs[r], I, fp8)
+                a = _swiglu_then_requant(wgu @ xs[r], I, fp8, gate)
                 acc[r] += ws[r, j] * (wd @ a)
     elif mode == "fast":
         flat = ids.reshape(-1)
@@ -283,7 +303,7 @@ def forward(x: np.ndarray, idx: np.ndarray, w: np.ndarray, weights: ExpertWeight
             r_of, j_of = sl // k, sl % k
             wgu, wd = weights.gate_up_f64(int(e)), weights.down_f64(int(e))
             I = wd.shape[1]
-            a = _swiglu_then_requant(xs[r_of] @ wgu.T, I, fp8)
+            a = _swiglu_then_requant(xs[r_of] @ wgu.T, I, fp8, gate)
             y = a @ wd.T
             np.add.at(acc, r_of, ws[r_of, j_of][:, None] * y)
     else:

@@ -131,21 +131,53 @@ def test_fp8_dense_bruteforce(scale):
 
 # ----------------------------------------------------------------------------- special case
 
-def test_k1_unit_weight_is_dense_swiglu_mlp():
+TORCH_GATES = {"silu": torch.nn.functional.silu,
+               "gelu": lambda v: torch.nn.functional.gelu(v, approximate="none"),
+               "relu": torch.nn.functional.relu}
+
+
+@pytest.mark.parametrize("gate", ["silu", "gelu", "relu"])
+def test_k1_unit_weight_is_dense_gated_mlp(gate):
     spec = synth.Spec("k1", T=12, H=96, I=48, E=4, k=1, act="f32", weight="f32", seed=3)
     L = synth.dense_layer(spec)
     w1 = np.ones_like(L["w"])
-    acc, out = forward(L["x"], L["idx"], w1, _weights(L), act="f32")
+    acc, out = forward(L["x"], L["idx"], w1, _weights(L), act="f32", gate=gate)
     I = spec.I
     for t in range(spec.T):
         e = L["idx"][t, 0]
         W = torch.from_numpy(L["w_gate_up"][e].astype(np.float64))
-        gate, up = W[:I], W[I:]
+        wg, wu = W[:I], W[I:]
         xd = torch.from_numpy(L["x"][t].astype(np.float64))
-        h = torch.nn.functional.silu(torch.nn.functional.linear(xd, gate)) * \
-            torch.nn.functional.linear(xd, up)
+        h = TORCH_GATES[gate](torch.nn.functional.linear(xd, wg)) * torch.nn.functional.linear(xd, wu)
         y = torch.nn.functional.linear(h, torch.from_numpy(L["w_down"][e].astype(np.float64)))
         assert np.allclose(acc[t], y.numpy(), rtol=1e-13, atol=1e-14)
+
+
+def test_gelu_and_relu_gates():
+    from oracle.moe import gelu, relu
+    # Phi(1) and Phi(-1) of the standard normal CDF
+    assert gelu(np.array([1.0]))[0] == pytest.approx(0.8413447460685429, rel=1e-15)
+    assert gelu(np.array([-1.0]))[0] == pytest.approx(-0.15865525393145707, rel=1e-14)
+    assert gelu(np.array([0.0]))[0] == 0.0
+    zz = np.linspace(-30, 30, 601)
+    # Phi(z) + Phi(-z) = 1  =>  gelu(z) - gelu(-z) = z
+    assert np.allclose(gelu(zz) - gelu(-zz), zz, rtol=0, atol=1e-13)
+    # library routine (its 1 + erf form rounds the far negative tail to 0, hence the atol)
+    assert np.allclose(gelu(zz), torch.nn.functional.gelu(torch.from_numpy(zz), approximate="none").numpy(),
+                       rtol=1e-13, atol=1e-15)
+    assert (relu(zz) == np.where(zz > 0, zz, 0.0)).all()
+
+
+def test_gated_literal_equals_fast():
+    spec = synth.Spec("g", T=10, H=64, I=32, E=5, k=3, act="f32", weight="f32", seed=9)
+    L = synth.dense_layer(spec)
+    W = _weights(L)
+    for gate in ("gelu", "relu"):
+        a1, _ = forward(L["x"], L["idx"], L["w"], W, act="f32", mode="literal", gate=gate)
+        a2, _ = forward(L["x"], L["idx"], L["w"], W, act="f32", mode="fast", gate=gate)
+        assert np.allclose(a1, a2, rtol=1e-12, atol=1e-14)
+        a3, _ = forward(L["x"], L["idx"], L["w"], W, act="f32", gate="silu")
+        assert not np.allclose(a1, a3)          # the gate is really applied
 
 
 # ----------------------------------------------------------------------------- invariants
