@@ -78,7 +78,13 @@ enum {
   MOE_FLAG_FORCE_DECODE = 8u,
   /* Combine with floating-point atomic adds into a float32 [T, H] accumulator at
    * every size (the smaller workspace); not with MOE_FLAG_DETERMINISTIC. */
-  MOE_FLAG_ATOMIC_COMBINE = 16u
+  MOE_FLAG_ATOMIC_COMBINE = 16u,
+  /* The gated activation a = gate(g) * u of the expert MLP (SonicMoE section: gated
+   * activations silu, gelu or relu map to SwiGLU, GeGLU or ReGLU).  Default: SwiGLU,
+   * gate = silu.  GELU: gate = GELU in its exact form z * Phi(z).  RELU: gate =
+   * max(z, 0).  At most one of the two. */
+  MOE_FLAG_ACT_GELU = 32u,
+  MOE_FLAG_ACT_RELU = 64u
 };
 
 /* Problem description (plain values; no pointers). */

@@ -17,7 +17,7 @@ import torch
 
 __all__ = [
     "experts_forward", "route", "route_logits", "quantize_rows_fp8", "workspace_size", "plan_describe",
-    "Problem", "MoeError", "lib", "FLAG_CHECK_INDICES", "FLAG_DETERMINISTIC", "FLAG_ATOMIC_COMBINE",
+    "Problem", "MoeError", "lib", "FLAG_CHECK_INDICES", "FLAG_DETERMINISTIC", "FLAG_ATOMIC_COMBINE", "FLAG_ACT_GELU", "FLAG_ACT_RELU",
     "FLAG_FORCE_GROUPED", "FLAG_FORCE_DECODE", "LIB_PATH",
 ]
 
@@ -35,6 +35,8 @@ FLAG_DETERMINISTIC = 2
 FLAG_FORCE_GROUPED = 4
 FLAG_FORCE_DECODE = 8
 FLAG_ATOMIC_COMBINE = 16
+FLAG_ACT_GELU = 32
+FLAG_ACT_RELU = 64
 
 EXPORTS = ["moe_abi_version", "moe_status_str", "moe_workspace_size", "moe_experts_forward",
            "moe_route", "moe_route_logits", "moe_quantize_rows_fp8", "moe_plan_describe",

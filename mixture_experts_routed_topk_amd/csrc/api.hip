@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include "../../include/moe_experts.h"
+#include "device_common.h"
 #include "internal.h"
 
 namespace moe {
@@ -35,10 +36,12 @@ moe_status validate_problem(const moe_problem* p) {
                          (p->scale_fmt == MOE_SCALE_F32 || p->scale_fmt == MOE_SCALE_UE8M0);
   if (!(combo_f32 || combo_bf16 || combo_fp8)) return MOE_ERR_UNSUPPORTED;
   const uint32_t known = MOE_FLAG_CHECK_INDICES | MOE_FLAG_DETERMINISTIC | MOE_FLAG_FORCE_GROUPED |
-                         MOE_FLAG_FORCE_DECODE | MOE_FLAG_ATOMIC_COMBINE;
+                         MOE_FLAG_FORCE_DECODE | MOE_FLAG_ATOMIC_COMBINE | MOE_FLAG_ACT_GELU |
+                         MOE_FLAG_ACT_RELU;
   if (p->flags & ~known) return MOE_ERR_UNSUPPORTED;
   if ((p->flags & MOE_FLAG_FORCE_GROUPED) && (p->flags & MOE_FLAG_FORCE_DECODE)) return MOE_ERR_UNSUPPORTED;
   if ((p->flags & MOE_FLAG_DETERMINISTIC) && (p->flags & MOE_FLAG_ATOMIC_COMBINE)) return MOE_ERR_UNSUPPORTED;
+  if ((p->flags & MOE_FLAG_ACT_GELU) && (p->flags & MOE_FLAG_ACT_RELU)) return MOE_ERR_UNSUPPORTED;
   if (p->T < 0 || p->E < 1 || p->E > 1024 || p->k < 1 || p->k > p->E) return MOE_ERR_BAD_SHAPE;
   if (p->H <= 0 || p->I <= 0 || p->H > 65536 || p->I > 65536) return MOE_ERR_BAD_SHAPE;
   if (p->H % 128 != 0) return MOE_ERR_BAD_SHAPE;
@@ -230,8 +233,9 @@ moe_status moe_plan_describe(const moe_problem* p, char* buf, size_t len) {
                      : p->weight_dtype == MOE_F32 ? "fma_64x64"
                      : p->weight_dtype == MOE_BF16 ? "mfma32x32x16_bf16_160x256_k64_lds_dma_ring3"
                                                    : "gateup_mfma32x32x16_widened_e4m3_160x128_ring4+down_mfma16x16x128_e4m3_128x256_ring3";
-  snprintf(buf, len, "path=%s weights=%s scales=%s kernels=%s combine=%s workspace_bytes=%zu",
-           pl.path == kDecode ? "decode" : "grouped", wname, sname, kern,
+  const char* gname = (p->flags & MOE_FLAG_ACT_GELU) ? "geglu" : ((p->flags & MOE_FLAG_ACT_RELU) ? "reglu" : "swiglu");
+  snprintf(buf, len, "path=%s weights=%s scales=%s kernels=%s activation=%s combine=%s workspace_bytes=%zu",
+           pl.path == kDecode ? "decode" : "grouped", wname, sname, kern, gname,
            slot_combine(*p) ? "slot_rows" : "atomic_f32", L.total);
   return MOE_OK;
 }
@@ -382,6 +386,7 @@ moe_status moe_experts_forward(const moe_problem* p, const void* hidden, const i
 
   GroupedArgs g{};
   g.E = p->E;
+  g.gate = (p->flags & MOE_FLAG_ACT_GELU) ? kGateGelu : ((p->flags & MOE_FLAG_ACT_RELU) ? kGateRelu : kGateSilu);
   g.offsets = offsets;
   g.mt = mt;
   g.I = p->I;

@@ -85,8 +85,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(GroupedArgs g) {
         const int col0 = cb * 64 + wave * 16 + 4 * grp;
         if (MODE == kGateUp) {
           uint16_t* o = static_cast<uint16_t*>(g.act_out) + (int64_t)p * g.I + col0;
-          const uint32_t lo = pack_bf16x2(silu_fast(accg[0]) * accu[0], silu_fast(accg[1]) * accu[1]);
-          const uint32_t hi = pack_bf16x2(silu_fast(accg[2]) * accu[2], silu_fast(accg[3]) * accu[3]);
+          const uint32_t lo = pack_bf16x2(gate_fn<true>(g.gate, accg[0]) * accu[0], gate_fn<true>(g.gate, accg[1]) * accu[1]);
+          const uint32_t hi = pack_bf16x2(gate_fn<true>(g.gate, accg[2]) * accu[2], gate_fn<true>(g.gate, accg[3]) * accu[3]);
           *reinterpret_cast<uint2*>(o) = make_uint2(lo, hi);
         } else {
           const int slot = g.perm[p];

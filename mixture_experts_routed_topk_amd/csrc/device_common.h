@@ -54,6 +54,20 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
 
 __device__ __forceinline__ float silu_fast(float z) { return z / (1.0f + __expf(-z)); }
 __device__ __forceinline__ float silu_exact(float z) { return z / (1.0f + expf(-z)); }
+// GELU in its exact form z * Phi(z) = z / 2 * erfc(-z / sqrt 2) (erfc keeps the far negative
+// tail accurate), and ReLU: the gates of GeGLU and ReGLU
+__device__ __forceinline__ float gelu_exact(float z) { return 0.5f * z * erfcf(-0.70710678118654752f * z); }
+__device__ __forceinline__ float relu_gate(float z) { return z > 0.0f ? z : 0.0f; }
+
+// The gate function of the gated activation a = gate(g) * u: SwiGLU (silu, the default),
+// GeGLU (gelu) or ReGLU (relu).  FAST: silu on the hardware exp (for bf16 results).
+enum { kGateSilu = 0, kGateGelu = 1, kGateRelu = 2 };
+template <bool FAST>
+__device__ __forceinline__ float gate_fn(int gate, float z) {
+  if (gate == kGateGelu) return gelu_exact(z);
+  if (gate == kGateRelu) return relu_gate(z);
+  return FAST ? silu_fast(z) : silu_exact(z);
+}
 
 // ---------------------------------------------------------------------------- MFMA
 

@@ -274,7 +274,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_bf16_kernel(GroupedArgs g
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int r = (2 * i + wm) * 32 + 8 * (v >> 2) + 4 * hgrp + (v & 3);
-          const float a = silu_fast(acc[i][0][v]) * acc[i][1][v];
+          const float a = gate_fn<true>(g.gate, acc[i][0][v]) * acc[i][1][v];
           stage[r * 128 + wn * 32 + r32] = (uint16_t)f32_to_bf16_bits(a);
         }
       }

@@ -74,7 +74,7 @@ __global__ __launch_bounds__(kThreads) void gateup_f32_kernel(GroupedArgs g) {
     if (r < it.rows) {
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        out[(int64_t)(it.row0 + r) * g.I + it.nt * BNG + tx + 16 * j] = silu_exact(gt[i][j]) * up[i][j];
+        out[(int64_t)(it.row0 + r) * g.I + it.nt * BNG + tx + 16 * j] = gate_fn<false>(g.gate, gt[i][j]) * up[i][j];
     }
   }
 }

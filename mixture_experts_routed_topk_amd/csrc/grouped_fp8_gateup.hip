@@ -287,7 +287,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_fp8_gateup_kernel(Grouped
       for (int v = 0; v < 16; ++v) {
         const float up = __shfl_xor(acc[i][v], 16);
         const int r = (2 * i + wm) * 32 + 8 * (v >> 2) + 4 * hgrp + (v & 3);
-        if (!(lane & 16) && r < rows) out[(int64_t)(row0 + r) * g.I + col] = silu_exact(acc[i][v]) * up;
+        if (!(lane & 16) && r < rows) out[(int64_t)(row0 + r) * g.I + col] = gate_fn<false>(g.gate, acc[i][v]) * up;
       }
     }
     __syncthreads();   // the ring and sSb are reused by the next item

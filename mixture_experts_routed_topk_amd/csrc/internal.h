@@ -76,6 +76,7 @@ struct GroupedArgs {
   // accumulator the down kernel adds into), or nothing when zero_out is null
   float* zero_out;
   int64_t zero_n4;
+  int gate;                 // gate function of the gated activation (kGate*)
 };
 
 // Upper bound on M tiles for a tile height (host-side grid sizing).

@@ -40,9 +40,9 @@ def prefetched_weights(spec: synth.Spec, experts, threads: int = 16) -> ExpertWe
     return ExpertWeights(spec.weight, lambda e: gu[e], lambda e: dn[e])
 
 
-def oracle_out(spec, x, idx, w, weights, tokens=None, mode="fast"):
+def oracle_out(spec, x, idx, w, weights, tokens=None, mode="fast", gate="silu"):
     """Oracle result (rounded to the output type) as fp64, for all tokens or a subset."""
-    _, out = forward(x, idx, w, weights, act=spec.act, E=spec.E, mode=mode, tokens=tokens)
+    _, out = forward(x, idx, w, weights, act=spec.act, E=spec.E, mode=mode, tokens=tokens, gate=gate)
     return out_as_f64(out, spec.act)
 
 

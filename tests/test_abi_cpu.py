@@ -63,7 +63,10 @@ def _ws(p):
     (dict(act=m.BF16, weight=m.BF16, scale=m.SCALE_F32), m.ERR_UNSUPPORTED),
     (dict(act=m.F32, weight=m.FP8_E4M3, scale=m.SCALE_F32), m.ERR_UNSUPPORTED),
     (dict(flags=m.FLAG_FORCE_DECODE | m.FLAG_FORCE_GROUPED), m.ERR_UNSUPPORTED),
-    (dict(flags=64), m.ERR_UNSUPPORTED),
+    (dict(flags=128), m.ERR_UNSUPPORTED),
+    (dict(flags=m.FLAG_ACT_GELU | m.FLAG_ACT_RELU), m.ERR_UNSUPPORTED),
+    (dict(flags=m.FLAG_ACT_GELU), m.OK),
+    (dict(flags=m.FLAG_ACT_RELU), m.OK),
 ])
 def test_problem_validation(kw, status):
     st, n = _ws(P(**kw))

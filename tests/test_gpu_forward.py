@@ -37,7 +37,8 @@ def _full_check(spec, flags, tokens=None, what=""):
     out = gpu_out_f64(_run(D, flags))
     rows = np.arange(spec.T) if tokens is None else tokens
     W = prefetched_weights(spec, np.unique(D["idx_host"][rows]))
-    ref = oracle_out(spec, D["x_host"], D["idx_host"], D["w_host"], W, tokens=tokens)
+    gate = "gelu" if flags & m.FLAG_ACT_GELU else ("relu" if flags & m.FLAG_ACT_RELU else "silu")
+    ref = oracle_out(spec, D["x_host"], D["idx_host"], D["w_host"], W, tokens=tokens, gate=gate)
     got = out if tokens is None else out[tokens]
     print(f"{what or spec.name} flags={flags}: T={spec.T} active={len(D['active'])}")
     return assert_close(got, ref, spec.act, what or spec.name)
@@ -215,3 +216,26 @@ def test_quantize_rows_config_hidden_bit_exact():
     rq, rs = quant_rows(bf16_bits_to_f64(xh).astype(np.float32))
     assert np.array_equal(q.cpu().numpy(), rq)
     assert np.array_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+
+
+# ----------------------------------------------------------------------------- GeGLU / ReGLU
+
+GATED_CASES = {
+    "bf16_grouped": (dict(T=300, H=256, I=192, E=7, k=3, act="bf16", weight="bf16"), m.FLAG_FORCE_GROUPED),
+    "bf16_decode": (dict(T=40, H=256, I=256, E=6, k=2, act="bf16", weight="bf16"), m.FLAG_FORCE_DECODE),
+    "f32": (dict(T=200, H=128, I=64, E=5, k=2, act="f32", weight="f32"), m.FLAG_FORCE_GROUPED),
+    "fp8": (dict(T=200, H=256, I=256, E=5, k=2, act="bf16", weight="fp8", scale="f32"), 0),
+}
+
+
+@pytest.mark.parametrize("gate", ["gelu", "relu"])
+@pytest.mark.parametrize("case", list(GATED_CASES))
+def test_gated_activations(gate, case):
+    shape, flags = GATED_CASES[case]
+    spec = synth.Spec(f"gated_{case}", renorm=True, seed=13, **shape)
+    gflag = m.FLAG_ACT_GELU if gate == "gelu" else m.FLAG_ACT_RELU
+    D = device_layer(spec)
+    prob = m.problem_for(D["x"], D["idx"], D["w_gate_up"], D["w_down"],
+                         D.get("w_gate_up_scale"), flags | gflag)
+    assert ("activation=geglu" if gate == "gelu" else "activation=reglu") in m.plan_describe(prob)
+    _full_check(spec, flags | gflag, what=f"{case} {gate}")
