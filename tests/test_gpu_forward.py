@@ -239,3 +239,25 @@ def test_gated_activations(gate, case):
                          D.get("w_gate_up_scale"), flags | gflag)
     assert ("activation=geglu" if gate == "gelu" else "activation=reglu") in m.plan_describe(prob)
     _full_check(spec, flags | gflag, what=f"{case} {gate}")
+
+
+# ----------------------------------------------------------------------------- limits
+
+@pytest.mark.parametrize("weight", ["bf16", "fp8"])
+def test_max_experts(weight):
+    # E at the library's maximum (1024): most experts empty, 16-bit M-tile tables in LDS
+    shape = dict(T=700, H=256, I=128, E=1024, k=8) if weight == "bf16" else dict(T=300, H=256, I=128, E=1024, k=4)
+    extra = dict(scale="ue8m0") if weight == "fp8" else {}
+    spec = synth.Spec(f"maxE_{weight}", act="bf16", weight=weight, renorm=True, seed=17, **shape, **extra)
+    _full_check(spec, m.FLAG_FORCE_GROUPED | m.FLAG_ATOMIC_COMBINE)
+    _full_check(spec, m.FLAG_FORCE_GROUPED)
+
+
+@pytest.mark.parametrize("weight", ["bf16", "fp8"])
+def test_wide_hidden(weight):
+    # a long K loop in gate_up (H = 16384: 256 bf16 slices / 128 e4m3 scale blocks) and
+    # 64 output tiles in down
+    extra = dict(scale="f32") if weight == "fp8" else {}
+    spec = synth.Spec(f"wideH_{weight}", T=96, H=16384, I=128, E=4, k=2, act="bf16", weight=weight,
+                      renorm=True, seed=19, **extra)
+    _full_check(spec, m.FLAG_FORCE_GROUPED)
