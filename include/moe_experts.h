@@ -116,8 +116,10 @@ const char* moe_status_str(moe_status s);
  * closed form, no HIP call).  Grows with T*k*(I + H) and T*H.  When the k rows of a
  * token are combined as per-slot rows (always with MOE_FLAG_DETERMINISTIC; by default
  * while 4*T*k*H <= 512 MiB, where that combine is the faster one; never with
- * MOE_FLAG_ATOMIC_COMBINE) it holds a float32 [T*k, H] buffer instead of the float32
- * [T, H] accumulator. */
+ * MOE_FLAG_ATOMIC_COMBINE) it holds a [T*k, H] buffer instead of the float32 [T, H]
+ * accumulator: float32 rows with MOE_FLAG_DETERMINISTIC, and bf16 rows (each slot's
+ * weighted row rounded once, the k rows summed in float32) on the default bf16
+ * grouped path. */
 moe_status moe_workspace_size(const moe_problem* p, size_t* bytes);
 
 /*

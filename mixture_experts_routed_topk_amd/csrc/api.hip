@@ -86,6 +86,17 @@ bool slot_combine(const moe_problem& p) {
   return 4 * (int64_t)p.T * p.k * p.H <= kSlotCombineMaxBytes;
 }
 
+// The per-slot rows of the bf16 grouped path's default combine are stored as bf16: each
+// slot's weighted row is rounded once to bf16 and the k rows of a token are summed in
+// float32 (MOE_FLAG_DETERMINISTIC keeps float32 rows).  On the Qwen prefill layer this
+// moves half the bytes of float32 rows; the extra rounding stays far inside the bf16
+// tolerance (simulated on sampled tokens: worst error 0.12 of the tolerance, against
+// 0.065 with float32 rows).
+bool slot_rows_bf16(const moe_problem& p, bool decode) {
+  return slot_combine(p) && !(p.flags & MOE_FLAG_DETERMINISTIC) && !decode && p.weight_dtype == MOE_BF16 &&
+         p.act_dtype == MOE_BF16;
+}
+
 bool decode_capable(const moe_problem& p) { return p.weight_dtype == MOE_BF16 && p.I % 128 == 0; }
 
 Plan make_plan(const moe_problem& p) {
@@ -140,7 +151,8 @@ Layout make_layout(const moe_problem& p) {
   L.x_s = fp8 ? take(4 * T * (H / 128)) : o;
   const bool det = slot_combine(p);
   L.acc = det ? o : take(4 * T * H);
-  L.slots = det ? take(4 * A * H) : o;
+  const bool rows16 = slot_rows_bf16(p, make_plan(p).path == kDecode);
+  L.slots = det ? take((rows16 ? 2 : 4) * A * H) : o;
   L.total = o;
   return L;
 }
@@ -236,7 +248,8 @@ moe_status moe_plan_describe(const moe_problem* p, char* buf, size_t len) {
   const char* gname = (p->flags & MOE_FLAG_ACT_GELU) ? "geglu" : ((p->flags & MOE_FLAG_ACT_RELU) ? "reglu" : "swiglu");
   snprintf(buf, len, "path=%s weights=%s scales=%s kernels=%s activation=%s combine=%s workspace_bytes=%zu",
            pl.path == kDecode ? "decode" : "grouped", wname, sname, kern, gname,
-           slot_combine(*p) ? "slot_rows" : "atomic_f32", L.total);
+           slot_combine(*p) ? (slot_rows_bf16(*p, pl.path == kDecode) ? "slot_rows_bf16" : "slot_rows_f32")
+                            : "atomic_f32", L.total);
   return MOE_OK;
 }
 
@@ -353,6 +366,7 @@ moe_status moe_experts_forward(const moe_problem* p, const void* hidden, const i
   int32_t* inv = reinterpret_cast<int32_t*>(ws + L.inv);
   float* acc = det ? nullptr : reinterpret_cast<float*>(ws + L.acc);
   float* slots = det ? reinterpret_cast<float*>(ws + L.slots) : nullptr;
+  const bool rows16 = slot_rows_bf16(*p, pl.path == kDecode);   // (slots then holds bf16 bits)
 
   // the atomic combine adds into a cleared float32 accumulator; the bf16 grouped
   // gate_up kernel clears it itself after its tiles, other paths launch a fill
@@ -396,6 +410,7 @@ moe_status moe_experts_forward(const moe_problem* p, const void* hidden, const i
   g.topk_w = topk_w;
   g.acc_out = acc;
   g.slot_out = slots;
+  g.slot_bf16 = rows16;
   g.b_scale_ue8m0 = p->scale_fmt == MOE_SCALE_UE8M0;
 
   // gate_up + SwiGLU: rows = hidden rows gathered through perm (token = slot / k)
@@ -479,7 +494,10 @@ moe_status moe_experts_forward(const moe_problem* p, const void* hidden, const i
 
   const int out_bf16 = p->act_dtype == MOE_BF16;
   MOE_HIP_CHECK(stage_mark(MOE_STAGE_FINALIZE, 0, s));
-  if (det) MOE_HIP_CHECK(launch_finalize_slots(slots, inv, out, p->T, p->k, p->H, out_bf16, s));
+  if (det && rows16)
+    MOE_HIP_CHECK(launch_finalize_slots_bf16(reinterpret_cast<const uint16_t*>(slots), inv, out, p->T, p->k, p->H,
+                                             out_bf16, s));
+  else if (det) MOE_HIP_CHECK(launch_finalize_slots(slots, inv, out, p->T, p->k, p->H, out_bf16, s));
   else MOE_HIP_CHECK(launch_finalize_acc(acc, out, p->T, p->H, out_bf16, s));
   MOE_HIP_CHECK(stage_mark(MOE_STAGE_FINALIZE, 1, s));
 

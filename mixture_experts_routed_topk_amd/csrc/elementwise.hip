@@ -36,7 +36,21 @@ __global__ __launch_bounds__(kThreads) void finalize_acc_kernel(const float4* __
   }
 }
 
-__global__ __launch_bounds__(kThreads) void finalize_slots_kernel(const float* __restrict__ rows,
+// 8 consecutive values of a slot row (float32 or bf16 bits) as float32
+__device__ __forceinline__ void load8(const float* rows, int64_t at, float* v) {
+  const float4* r = reinterpret_cast<const float4*>(rows + at);
+  const float4 a = r[0], b = r[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void load8(const uint16_t* rows, int64_t at, float* v) {
+  const uint4 q = *reinterpret_cast<const uint4*>(rows + at);
+  v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x); v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
+  v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z); v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
+}
+
+template <typename R>
+__global__ __launch_bounds__(kThreads) void finalize_slots_kernel(const R* __restrict__ rows,
                                                                   const int32_t* __restrict__ inv, void* out,
                                                                   int64_t T, int k, int H, int out_bf16) {
   const int h8 = H / 8;
@@ -49,10 +63,10 @@ __global__ __launch_bounds__(kThreads) void finalize_slots_kernel(const float* _
     for (int j = 0; j < k; ++j) {
       const int64_t slot = t * k + j;
       if (inv[slot] < 0) continue;
-      const float4* r = reinterpret_cast<const float4*>(rows + slot * H + c);
-      const float4 a = r[0], b = r[1];
-      s[0] += a.x; s[1] += a.y; s[2] += a.z; s[3] += a.w;
-      s[4] += b.x; s[5] += b.y; s[6] += b.z; s[7] += b.w;
+      float v[8];
+      load8(rows, slot * H + c, v);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) s[q] += v[q];
     }
     if (out_bf16) {
       uint4 o;
@@ -93,8 +107,16 @@ hipError_t launch_finalize_acc(const float* acc, void* out, int64_t T, int H, in
 hipError_t launch_finalize_slots(const float* slot_rows, const int32_t* inv, void* out, int64_t T, int k, int H,
                                  int out_bf16, hipStream_t s) {
   const int64_t n8 = T * (H / 8);
-  hipLaunchKernelGGL(finalize_slots_kernel, dim3(grid_for(n8)), dim3(kThreads), 0, s, slot_rows, inv, out, T, k, H,
-                     out_bf16);
+  hipLaunchKernelGGL(finalize_slots_kernel<float>, dim3(grid_for(n8)), dim3(kThreads), 0, s, slot_rows, inv, out, T,
+                     k, H, out_bf16);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize_slots_bf16(const uint16_t* slot_rows, const int32_t* inv, void* out, int64_t T, int k,
+                                      int H, int out_bf16, hipStream_t s) {
+  const int64_t n8 = T * (H / 8);
+  hipLaunchKernelGGL(finalize_slots_kernel<uint16_t>, dim3(grid_for(n8)), dim3(kThreads), 0, s, slot_rows, inv, out,
+                     T, k, H, out_bf16);
   return hipGetLastError();
 }
 

@@ -62,7 +62,7 @@ constexpr int BLD = BN / RPI / NW;        // B DMA instructions per wave per sli
 constexpr int kMaxE = 1024;
 static_assert(ALD <= KSTEPS && BLD == KSTEPS, "the DMA of a slice is spread one A and one B block per k step");
 
-enum { kGateUp = 0, kDownAtomic = 1, kDownSlots = 2 };
+enum { kGateUp = 0, kDownAtomic = 1, kDownSlots = 2, kDownSlotsBf16 = 3 };
 
 // LDS chunk slot of logical 16-byte chunk c of tile row `row`: the 16 rows of a 16-lane
 // fragment-read group land in 16 distinct 16-byte bank groups of a 256-byte window
@@ -307,6 +307,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_bf16_kernel(GroupedArgs g
             const int col = nt * BN + tile_col0(j) + r32;
             if (col < ncols) {
               if (MODE == kDownAtomic) unsafeAtomicAdd(g.acc_out + tok * g.H + col, wt * acc[i][j][v]);
+              else if (MODE == kDownSlotsBf16)
+                reinterpret_cast<uint16_t*>(g.slot_out)[tok * g.H + col] = (uint16_t)f32_to_bf16_bits(wt * acc[i][j][v]);
               else g.slot_out[tok * g.H + col] = wt * acc[i][j][v];
             }
           }
@@ -344,7 +346,8 @@ int down_bf16_cols() { return BN; }
 hipError_t launch_gateup_bf16(const GroupedArgs& g, int grid, hipStream_t s) { return launch<kGateUp>(g, grid, s); }
 
 hipError_t launch_down_bf16(const GroupedArgs& g, int grid, hipStream_t s) {
-  return g.slot_out ? launch<kDownSlots>(g, grid, s) : launch<kDownAtomic>(g, grid, s);
+  if (!g.slot_out) return launch<kDownAtomic>(g, grid, s);
+  return g.slot_bf16 ? launch<kDownSlotsBf16>(g, grid, s) : launch<kDownSlots>(g, grid, s);
 }
 
 }  // namespace moe

@@ -71,7 +71,8 @@ struct GroupedArgs {
   int k;
   int H;
   float* acc_out;           // [T][H] float32 accumulator (atomic combine), or
-  float* slot_out;          // [A][H] float32 per-slot rows (deterministic combine)
+  float* slot_out;          // [A][H] per-slot rows (per-slot combine): float32, or bf16
+  int slot_bf16;            //   bits when slot_bf16 (bf16 down kernel only)
   // bf16 gate_up only: clear zero_n4 float4s at zero_out after its last tile (the
   // accumulator the down kernel adds into), or nothing when zero_out is null
   float* zero_out;
@@ -124,5 +125,7 @@ hipError_t launch_finalize_acc(const float* acc, void* out, int64_t T, int H, in
 // out[t][h] = round(sum_j slot_rows[t*k + j][h]) over slots with inv != -1, in slot order
 hipError_t launch_finalize_slots(const float* slot_rows, const int32_t* inv, void* out, int64_t T,
                                  int k, int H, int out_bf16, hipStream_t s);
+hipError_t launch_finalize_slots_bf16(const uint16_t* slot_rows, const int32_t* inv, void* out, int64_t T,
+                                      int k, int H, int out_bf16, hipStream_t s);
 
 }  // namespace moe

@@ -84,8 +84,9 @@ def test_workspace_by_combine():
     _, n_atomic = _ws(p)
     p.flags = m.FLAG_DETERMINISTIC
     _, n_det = _ws(p)
-    assert n_det == n_default
-    assert n_det - n_atomic == 4 * 4096 * 4 * 2048 - 4 * 4096 * 2048
+    A, H, T = 4096 * 4, 2048, 4096
+    assert n_det - n_default == 2 * A * H        # default: bf16 slot rows; deterministic: float32
+    assert n_det - n_atomic == 4 * A * H - 4 * T * H
     # above 512 MiB of slot rows the default is the atomic combine
     big = P(act=m.BF16, weight=m.BF16, T=8192, H=7168, I=2048, E=256, k=8)
     _, nb_default = _ws(big)

@@ -20,6 +20,7 @@ pytestmark = pytest.mark.gpu
 # "grouped": expert-sorted grouped GEMMs with the float-atomic combine; "det": the same
 # with per-slot rows summed in slot order (also the default combine for small layers)
 PATHS = {"default": 0, "grouped": m.FLAG_FORCE_GROUPED | m.FLAG_ATOMIC_COMBINE,
+         "slots": m.FLAG_FORCE_GROUPED,   # default combine of small layers (bf16 rows for bf16)
          "det": m.FLAG_DETERMINISTIC | m.FLAG_FORCE_GROUPED}
 
 
@@ -49,7 +50,7 @@ def test_tiny_fp32(path):
     _full_check(synth.spec_for("tiny_fp32"), PATHS[path])
 
 
-@pytest.mark.parametrize("path", ["grouped", "det"])
+@pytest.mark.parametrize("path", ["grouped", "slots", "det"])
 @pytest.mark.parametrize("shape", [
     dict(T=300, H=256, I=192, E=7, k=3),      # several M tiles, ragged tails
     dict(T=1, H=128, I=64, E=4, k=2),
