@@ -25,6 +25,14 @@ The quantisation points are part of the result: the hidden states are quantised
 before the gate/up projection, and the SwiGLU output, rounded to fp32, is
 quantised before the down projection.
 
+FP4 experts (same section: weights packed two e2m1 codes per int8 byte, UE8M0 weight
+scales, DeepSeek-V4 style checkpoints): the pages fix neither the scale block nor the
+nibble order nor the activation format.  Taken here: one UE8M0 scale per row and per
+32 consecutive input channels (the OCP MX block, which also expresses any coarser
+block scaling exactly by repetition), element 2j in the low nibble of byte j, and
+activations quantised exactly as on the fp8 path.  Weight (r, c) dequantises to
+e2m1(code) * 2^(scale[r][c / 32] - 127).
+
 Two evaluation orders of the same definition:
   * literal: a loop over tokens and, inside, over the k chosen experts;
   * fast: expert-major, like the page's "eager" backend (loop over the selected
@@ -41,7 +49,9 @@ import numpy as np
 
 from .numerics import (
     bf16_bits_to_f64,
+    e2m1_decode,
     e4m3_decode,
+    fp4_unpack,
     f32_to_e4m3,
     f64_to_bf16_bits,
     f64_to_f32,
@@ -174,10 +184,11 @@ Storage = Union[np.ndarray, tuple]
 class ExpertWeights:
     """Expert weights in their storage format, dequantised to fp64 one expert at a time.
 
-    weight: "f32" | "bf16" | "fp8";  scale: "none" | "f32" | "ue8m0".
+    weight: "f32" | "bf16" | "fp8" | "fp4";  scale: "none" | "f32" | "ue8m0".
     gate_up / down: an indexable [E, ...] array (or a callable e -> matrix), in the
-    storage format: fp32 values, bf16 bit patterns, or e4m3 codes.  For fp8 the
-    matching scale arrays are [E, rows/128, cols/128] (or callables).
+    storage format: fp32 values, bf16 bit patterns, e4m3 codes, or packed e2m1 bytes
+    ([rows, cols/2]).  For fp8 the matching scale arrays are [E, rows/128, cols/128],
+    for fp4 they are UE8M0 bytes [E, rows, cols/32] (or callables).
     """
 
     weight: str
@@ -208,14 +219,28 @@ class ExpertWeights:
                 raise ValueError("block-scale shape mismatch")
             full = np.repeat(np.repeat(sv, 128, axis=0), 128, axis=1)
             return e4m3_decode(m) * full
+        if self.weight == "fp4":
+            if self.scale != "ue8m0":
+                raise ValueError("fp4 weights need UE8M0 scales")
+            codes = fp4_unpack(m)
+            R, C = codes.shape
+            sv = ue8m0_decode(s)
+            if sv.shape != (R, C // 32):
+                raise ValueError("fp4 scale shape mismatch")
+            return e2m1_decode(codes) * np.repeat(sv, 32, axis=1)
         raise ValueError(f"unknown weight format {self.weight!r}")
 
+    @property
+    def quantised(self) -> bool:
+        """fp8 and fp4 experts take e4m3 activations with dynamic per-row scales."""
+        return self.weight in ("fp8", "fp4")
+
     def gate_up_f64(self, e: int) -> np.ndarray:
-        s = self._get(self.gate_up_scale, e) if self.weight == "fp8" else None
+        s = self._get(self.gate_up_scale, e) if self.quantised else None
         return self._deq(self._get(self.gate_up, e), s)
 
     def down_f64(self, e: int) -> np.ndarray:
-        s = self._get(self.down_scale, e) if self.weight == "fp8" else None
+        s = self._get(self.down_scale, e) if self.quantised else None
         return self._deq(self._get(self.down, e), s)
 
 
@@ -273,7 +298,7 @@ def forward(x: np.ndarray, idx: np.ndarray, w: np.ndarray, weights: ExpertWeight
     idx = np.asarray(idx)
     T, k = idx.shape
     rows = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
-    fp8 = weights.weight == "fp8"
+    fp8 = weights.quantised          # e4m3 activations (fp8 and fp4 experts)
     if E is None and not callable(weights.gate_up):
         E = len(weights.gate_up)
     chosen = idx[rows]

@@ -6,9 +6,13 @@ e4m3  : OCP 8-bit floating point, E4M3 ("e4m3fn"): bias 7, 3 fraction bits,
         subnormals below 2^-6 with quantum 2^-9, largest finite 448 (0x7E),
         0x7F / 0xFF are NaN, no infinities.
 UE8M0 : unsigned 8-bit exponent-only scale, value 2^(b - 127), 0xFF is NaN.
+e2m1  : OCP 4-bit floating point (the MX element type FP4): 1 sign, 2 exponent bits
+        with bias 1, 1 fraction bit; exponent field 0 is subnormal (value m / 2);
+        no infinities or NaN, largest magnitude 6.  Two codes per byte.
 
 The Experts backends page ("FP8 and FP4 quantized experts" section and note) says
-fp8 experts come with float32 or UE8M0 block scales; these helpers decode both.
+fp8 experts come with float32 or UE8M0 block scales and FP4 experts come packed two
+codes per int8 with UE8M0 scales; these helpers decode all of them.
 Rounding is round-to-nearest-even throughout, done with np.rint on values scaled
 to an integer quantum (exact in fp64 for every case used here).
 """
@@ -91,6 +95,37 @@ def f32_to_e4m3(v: np.ndarray) -> np.ndarray:
     codes |= np.where(np.signbit(v), np.uint8(0x80), np.uint8(0))
     codes[np.isnan(v)] = np.uint8(0x7F)
     return codes
+
+
+def e2m1_value_table() -> np.ndarray:
+    """fp64 value of each of the 16 e2m1 codes, from the bit fields."""
+    vals = np.empty(16, dtype=np.float64)
+    for code in range(16):
+        sign = -1.0 if code & 0x8 else 1.0
+        ef = (code >> 1) & 0x3
+        m = code & 0x1
+        if ef == 0:
+            vals[code] = sign * (m / 2.0)                      # subnormal: 2^(1-1) * 0.m
+        else:
+            vals[code] = sign * (1.0 + m / 2.0) * 2.0 ** (ef - 1)
+    return vals
+
+
+_E2M1 = e2m1_value_table()
+
+
+def fp4_unpack(packed: np.ndarray) -> np.ndarray:
+    """Packed e2m1 bytes [..., C/2] -> codes [..., C]: byte j holds element 2j in its low
+    nibble and element 2j + 1 in its high nibble."""
+    b = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = b & 0x0F
+    out[..., 1::2] = b >> 4
+    return out
+
+
+def e2m1_decode(codes: np.ndarray) -> np.ndarray:
+    return _E2M1[np.asarray(codes, dtype=np.uint8) & 0x0F]
 
 
 def ue8m0_decode(b: np.ndarray) -> np.ndarray:

@@ -1,8 +1,9 @@
 """Stage a synthetic layer in GPU memory (torch tensors), expert by expert.
 
 Only the experts that received at least one slot are generated; every other
-expert is filled with NaN (bf16/fp32 NaN, e4m3 code 0x7F, NaN scales), so a
-kernel that touched an unselected expert would poison its output.  This also
+expert is filled with NaN (bf16/fp32 NaN, e4m3 code 0x7F, NaN scales; FP4 codes have
+no NaN, so there the UE8M0 scales 0xFF carry it), so a kernel that touched an
+unselected expert would poison its output.  This also
 keeps host memory and generation time proportional to the active experts.
 """
 
@@ -15,7 +16,7 @@ import torch
 
 from .layers import Spec, active_experts, expert_down, expert_gate_up, hidden, routing
 
-_TORCH_W = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
+_TORCH_W = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8, "fp4": torch.uint8}
 
 
 def host_to_tensor(a: np.ndarray, fmt: str) -> torch.Tensor:
@@ -28,6 +29,8 @@ def host_to_tensor(a: np.ndarray, fmt: str) -> torch.Tensor:
 def _poison(t: torch.Tensor, fmt: str):
     if fmt == "fp8":
         t.fill_(0x7F)
+    elif fmt == "fp4":
+        t.fill_(0x77)          # (6, 6); the NaN comes from the scales
     elif fmt == "ue8m0":
         t.fill_(0xFF)
     else:
@@ -50,10 +53,14 @@ def device_layer(spec: Spec, device="cuda", threads: int = 16, poison_inactive: 
     out["idx"] = torch.from_numpy(idx).to(device)
     out["w"] = torch.from_numpy(w).to(device)
     E, H, I = spec.E, spec.H, spec.I
-    gu = torch.empty((E, 2 * I, H), dtype=wdt, device=device)
-    dn = torch.empty((E, H, I), dtype=wdt, device=device)
-    fp8 = spec.weight == "fp8"
-    if fp8:
+    fp4 = spec.weight == "fp4"
+    gu = torch.empty((E, 2 * I, H // 2 if fp4 else H), dtype=wdt, device=device)
+    dn = torch.empty((E, H, I // 2 if fp4 else I), dtype=wdt, device=device)
+    fp8 = spec.weight in ("fp8", "fp4")     # (weights with scale tensors)
+    if fp4:
+        gus = torch.empty((E, 2 * I, H // 32), dtype=torch.uint8, device=device)
+        dns = torch.empty((E, H, I // 32), dtype=torch.uint8, device=device)
+    elif fp8:
         sdt = torch.float32 if spec.scale == "f32" else torch.uint8
         gus = torch.empty((E, 2 * I // 128, H // 128), dtype=sdt, device=device)
         dns = torch.empty((E, H // 128, I // 128), dtype=sdt, device=device)

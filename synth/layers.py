@@ -14,7 +14,11 @@ Everything here is input preparation:
     expert index, optional renormalisation, weights handed over as fp32;
   * expert weights: N(0, std = 1/sqrt(fan_in)) fp32 draws, stored as fp32, bf16,
     or OCP e4m3 codes with one scale per 128x128 block (float32 amax/448 scales or
-    UE8M0 power-of-two scales), the codes produced by torch's CPU float8 cast.
+    UE8M0 power-of-two scales), the codes produced by torch's CPU float8 cast;
+  * FP4 expert weights (DeepSeek-V4 style packing, two 4-bit codes per byte) are
+    drawn as codes directly: uniform random bytes, and one UE8M0 exponent per row and
+    32 input channels, uniform in [b0 - 1, b0 + 1] with b0 = 127 - 2 -
+    round(log2(sqrt(fan_in))), which keeps the weights' RMS near 1/sqrt(fan_in).
 
 Random streams: numpy PCG64 seeded through SeedSequence(seed).spawn(4) in the
 order hidden, logits, expert ranks, weights; the weights child spawns 2*E
@@ -40,8 +44,8 @@ class Spec:
     """One synthetic MoE layer.
 
     act:     "f32" | "bf16"            dtype of hidden and out
-    weight:  "f32" | "bf16" | "fp8"    storage of W_gate_up / W_down
-    scale:   "none" | "f32" | "ue8m0"  block-scale format (fp8 only)
+    weight:  "f32" | "bf16" | "fp8" | "fp4"  storage of W_gate_up / W_down
+    scale:   "none" | "f32" | "ue8m0"  block-scale format (fp8; fp4 takes ue8m0)
     routing: "normal" | "zipf"         router logits N(0,1), optionally + log-rank bias
     """
 
@@ -87,6 +91,10 @@ CONFIGS = {
     # Same layer with UE8M0 (power-of-two) block scales.
     "dsv3_fp8_ue8m0": Spec("dsv3_fp8_ue8m0", T=4096, H=7168, I=2048, E=256, k=8,
                            act="bf16", weight="fp8", scale="ue8m0", renorm=True,
+                           routing="zipf"),
+    # Same layer with FP4 (e2m1, two per byte) experts and UE8M0 scales per 1x32 block.
+    "dsv3_fp4_ue8m0": Spec("dsv3_fp4_ue8m0", T=4096, H=7168, I=2048, E=256, k=8,
+                           act="bf16", weight="fp4", scale="ue8m0", renorm=True,
                            routing="zipf"),
 }
 
@@ -214,7 +222,19 @@ def _block_quant(w: np.ndarray, fmt: str):
     return codes, scales
 
 
+def _fp4_codes(spec: Spec, e: int, which: int):
+    """Packed FP4 codes [rows, cols/2] and UE8M0 exponents [rows, cols/32] of one matrix."""
+    rows, cols = (2 * spec.I, spec.H) if which == 0 else (spec.H, spec.I)
+    rng = _rng(_weight_child(spec, e, which))
+    packed = rng.integers(0, 256, size=(rows, cols // 2), dtype=np.uint8)
+    b0 = 127 - 2 - int(round(math.log2(math.sqrt(cols))))
+    scales = rng.integers(b0 - 1, b0 + 2, size=(rows, cols // 32)).astype(np.uint8)
+    return packed, scales
+
+
 def _expert_matrix(spec: Spec, e: int, which: int):
+    if spec.weight == "fp4":
+        return _fp4_codes(spec, e, which)
     w = _draw(spec, e, which)
     if spec.weight == "f32":
         return w
@@ -228,7 +248,8 @@ def _expert_matrix(spec: Spec, e: int, which: int):
 def expert_gate_up(spec: Spec, e: int):
     """W_gate_up[e] [2I, H]: rows [0, I) gate, rows [I, 2I) up.
 
-    fp32 array, bf16 bits, or (e4m3 codes, scales [2I/128, H/128]) for fp8.
+    fp32 array, bf16 bits, (e4m3 codes, scales [2I/128, H/128]) for fp8, or
+    (packed e2m1 bytes [2I, H/2], UE8M0 scales [2I, H/32]) for fp4.
     """
     return _expert_matrix(spec, e, 0)
 
@@ -241,7 +262,7 @@ def expert_down(spec: Spec, e: int):
 def _stack(spec: Spec, fn, experts, threads: int):
     with ThreadPoolExecutor(max_workers=threads) as ex:
         parts = list(ex.map(lambda e: fn(spec, e), experts))
-    if spec.weight == "fp8":
+    if spec.weight in ("fp8", "fp4"):
         return (np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
     return np.stack(parts)
 
@@ -249,14 +270,14 @@ def _stack(spec: Spec, fn, experts, threads: int):
 def dense_layer(spec: Spec, threads: int = 8) -> dict:
     """All inputs as host arrays (for layers that fit comfortably in host RAM).
 
-    Keys: x, idx, w, w_gate_up, w_down, and for fp8 w_gate_up_scale, w_down_scale.
+    Keys: x, idx, w, w_gate_up, w_down, and for fp8 / fp4 w_gate_up_scale, w_down_scale.
     """
     idx, w = routing(spec)
     out = {"spec": spec, "x": hidden(spec), "idx": idx, "w": w}
     experts = range(spec.E)
     gu = _stack(spec, expert_gate_up, experts, threads)
     dn = _stack(spec, expert_down, experts, threads)
-    if spec.weight == "fp8":
+    if spec.weight in ("fp8", "fp4"):
         out["w_gate_up"], out["w_gate_up_scale"] = gu
         out["w_down"], out["w_down_scale"] = dn
     else:

@@ -17,8 +17,8 @@ def oracle_weights(spec: synth.Spec, layer: dict | None = None) -> ExpertWeights
     if layer is not None and "w_gate_up" in layer and isinstance(layer["w_gate_up"], np.ndarray):
         return ExpertWeights(spec.weight, layer["w_gate_up"], layer["w_down"], spec.scale,
                              layer.get("w_gate_up_scale"), layer.get("w_down_scale"))
-    if spec.weight == "fp8":
-        return ExpertWeights("fp8", lambda e: synth.expert_gate_up(spec, e)[0],
+    if spec.weight in ("fp8", "fp4"):
+        return ExpertWeights(spec.weight, lambda e: synth.expert_gate_up(spec, e)[0],
                              lambda e: synth.expert_down(spec, e)[0], spec.scale,
                              lambda e: synth.expert_gate_up(spec, e)[1],
                              lambda e: synth.expert_down(spec, e)[1])
@@ -34,8 +34,8 @@ def prefetched_weights(spec: synth.Spec, experts, threads: int = 16) -> ExpertWe
     with ThreadPoolExecutor(max_workers=threads) as ex:
         gu = dict(zip(experts, ex.map(lambda e: synth.expert_gate_up(spec, e), experts)))
         dn = dict(zip(experts, ex.map(lambda e: synth.expert_down(spec, e), experts)))
-    if spec.weight == "fp8":
-        return ExpertWeights("fp8", lambda e: gu[e][0], lambda e: dn[e][0], spec.scale,
+    if spec.weight in ("fp8", "fp4"):
+        return ExpertWeights(spec.weight, lambda e: gu[e][0], lambda e: dn[e][0], spec.scale,
                              lambda e: gu[e][1], lambda e: dn[e][1])
     return ExpertWeights(spec.weight, lambda e: gu[e], lambda e: dn[e])
 
