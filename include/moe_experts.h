@@ -50,13 +50,16 @@ typedef enum {
 typedef enum {
   MOE_F32 = 0,      /* IEEE binary32                                   */
   MOE_BF16 = 1,     /* bfloat16                                        */
-  MOE_FP8_E4M3 = 2  /* OCP 8-bit E4M3 ("e4m3fn": max 448, no infinity) */
+  MOE_FP8_E4M3 = 2, /* OCP 8-bit E4M3 ("e4m3fn": max 448, no infinity) */
+  MOE_FP4_E2M1 = 3  /* OCP 4-bit E2M1 (MX FP4: max 6), two codes per byte     */
 } moe_dtype;
 
 typedef enum {
   MOE_SCALE_NONE = 0,
-  MOE_SCALE_F32 = 1,   /* one float32 scale per 128x128 weight block               */
-  MOE_SCALE_UE8M0 = 2  /* one uint8 exponent b per block, scale = 2^(b-127)        */
+  MOE_SCALE_F32 = 1,   /* fp8: one float32 scale per 128x128 weight block          */
+  MOE_SCALE_UE8M0 = 2  /* one uint8 exponent b per block, scale = 2^(b-127); the
+                          block is 128x128 for fp8 weights and 1x32 (one weight
+                          row, 32 consecutive input channels) for fp4 weights      */
 } moe_scale_fmt;
 
 enum {
@@ -96,13 +99,15 @@ typedef struct {
   int32_t k;            /* experts per token, 1..E                                   */
   int32_t act_dtype;    /* moe_dtype of hidden and out: MOE_F32 or MOE_BF16          */
   int32_t weight_dtype; /* moe_dtype of the weights: MOE_F32 (with act MOE_F32),
-                           MOE_BF16 (with act MOE_BF16), MOE_FP8_E4M3 (act MOE_BF16) */
-  int32_t scale_fmt;    /* moe_scale_fmt: != NONE exactly when weights are fp8       */
+                           MOE_BF16 (with act MOE_BF16), MOE_FP8_E4M3 or
+                           MOE_FP4_E2M1 (act MOE_BF16)                               */
+  int32_t scale_fmt;    /* moe_scale_fmt: != NONE exactly when weights are fp8 or
+                           fp4; fp4 takes MOE_SCALE_UE8M0 only                       */
   uint32_t flags;       /* MOE_FLAG_*                                                */
 } moe_problem;
 
 /* Shape rules checked by every call taking a moe_problem:
- *   H % 128 == 0, I % 64 == 0 (f32, bf16 weights); H % 128 == 0, I % 128 == 0 (fp8);
+ *   H % 128 == 0, I % 64 == 0 (f32, bf16 weights); H % 128 == 0, I % 128 == 0 (fp8, fp4);
  *   1 <= E <= 1024, 1 <= k <= E, T * k < 2^31, H, I <= 65536, and each of hidden,
  *   the intermediate [T*k, I] rows and one expert's W_gate_up below 4 GiB.            */
 
@@ -134,6 +139,10 @@ moe_status moe_workspace_size(const moe_problem* p, size_t* bytes);
  *   w_down          [E, H, I]     weight_dtype
  *   w_gate_up_scale [E, 2I/128, H/128]  fp8 only: float32, or uint8 for UE8M0; NULL otherwise
  *   w_down_scale    [E, H/128, I/128]   fp8 only; NULL otherwise
+ *                   fp4 weights instead: w_gate_up [E, 2I, H/2] and w_down [E, H, I/2]
+ *                   uint8, byte j of a row holding element 2j in its low nibble and
+ *                   2j + 1 in its high nibble; UE8M0 scales w_gate_up_scale [E, 2I, H/32],
+ *                   w_down_scale [E, H, I/32] (uint8, 4-byte aligned)
  *   out             [T, H]        act_dtype; overwritten (never accumulated into)
  *   workspace       device scratch of workspace_bytes >= moe_workspace_size(p)
  *
@@ -142,6 +151,9 @@ moe_status moe_workspace_size(const moe_problem* p, size_t* bytes);
  * the bf16 hidden states are quantised per token and per 128 channels to e4m3
  * with a float32 scale amax/448, and so is the SwiGLU output before the down
  * projection; weight block (r, c) dequantises to code * scale[r/128][c/128].
+ * fp4 weights (same section: packed two per int8 with UE8M0 scales, DeepSeek-V4
+ * style): the activations are quantised exactly as for fp8, and weight (r, c)
+ * dequantises to e2m1(code) * 2^(scale[r][c/32] - 127).
  *
  * Returns MOE_OK once the work is enqueued (T == 0: nothing is enqueued).
  * Errors: NULL_ARG, BAD_SHAPE, UNSUPPORTED, WORKSPACE_TOO_SMALL before any HIP

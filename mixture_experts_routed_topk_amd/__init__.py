@@ -26,7 +26,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_expe
 # moe_status
 OK, ERR_NULL_ARG, ERR_BAD_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_BAD_INDEX, ERR_HIP = range(7)
 # moe_dtype
-F32, BF16, FP8_E4M3 = 0, 1, 2
+F32, BF16, FP8_E4M3, FP4_E2M1 = 0, 1, 2, 3
 # moe_scale_fmt
 SCALE_NONE, SCALE_F32, SCALE_UE8M0 = 0, 1, 2
 # flags
@@ -116,6 +116,7 @@ def _stream(device: torch.device):
 
 _ACT = {torch.float32: F32, torch.bfloat16: BF16}
 _WGT = {torch.float32: F32, torch.bfloat16: BF16, torch.float8_e4m3fn: FP8_E4M3, torch.uint8: FP8_E4M3}
+_FP4_DTYPES = (torch.float4_e2m1fn_x2,) if hasattr(torch, "float4_e2m1fn_x2") else ()
 
 
 def make_problem(T, H, I, E, k, act, weight, scale=SCALE_NONE, flags=0) -> Problem:
@@ -147,16 +148,20 @@ def problem_for(hidden, topk_idx, w_gate_up, w_down, w_gate_up_scale=None, flags
     T, H = hidden.shape
     E, twoI, H2 = w_gate_up.shape
     k = topk_idx.shape[1]
-    if H2 != H or twoI % 2 or tuple(w_down.shape) != (E, H, twoI // 2) or topk_idx.shape[0] != T:
+    # fp4 weights: packed bytes (uint8 or float4_e2m1fn_x2) with half as many columns
+    fp4 = (w_gate_up.dtype in _FP4_DTYPES or w_gate_up.dtype == torch.uint8) and 2 * H2 == H
+    cols = 2 if fp4 else 1
+    if (H2 * cols != H or twoI % 2 or tuple(w_down.shape) != (E, H, twoI // 2 // cols)
+            or topk_idx.shape[0] != T):
         raise ValueError("inconsistent shapes: hidden [T,H], topk_idx [T,k], "
-                         "w_gate_up [E,2I,H], w_down [E,H,I]")
-    if hidden.dtype not in _ACT or w_gate_up.dtype not in _WGT or w_down.dtype != w_gate_up.dtype:
+                         "w_gate_up [E,2I,H], w_down [E,H,I] (fp4: [E,2I,H/2], [E,H,I/2])")
+    if hidden.dtype not in _ACT or w_down.dtype != w_gate_up.dtype or not (fp4 or w_gate_up.dtype in _WGT):
         raise ValueError("unsupported dtypes")
-    weight = _WGT[w_gate_up.dtype]
+    weight = FP4_E2M1 if fp4 else _WGT[w_gate_up.dtype]
     scale = SCALE_NONE
-    if weight == FP8_E4M3:
+    if weight in (FP8_E4M3, FP4_E2M1):
         if w_gate_up_scale is None:
-            raise ValueError("fp8 weights need block scales")
+            raise ValueError("fp8 and fp4 weights need scales")
         scale = SCALE_UE8M0 if w_gate_up_scale.dtype == torch.uint8 else SCALE_F32
     return Problem(T, H, twoI // 2, E, k, _ACT[hidden.dtype], weight, scale, flags)
 
@@ -172,7 +177,9 @@ def experts_forward(hidden: torch.Tensor, topk_idx: torch.Tensor, topk_w: torch.
     hidden [T,H] f32|bf16; topk_idx [T,k] int32; topk_w [T,k] f32;
     w_gate_up [E,2I,H] and w_down [E,H,I] in f32 | bf16 | e4m3 (float8_e4m3fn or
     uint8 codes) with block scales [E,2I/128,H/128] / [E,H/128,I/128]
-    (float32, or uint8 UE8M0 exponents).
+    (float32, or uint8 UE8M0 exponents); or fp4: w_gate_up [E,2I,H/2] and
+    w_down [E,H,I/2] packed e2m1 bytes (uint8 or float4_e2m1fn_x2, element 2j in the low
+    nibble of byte j) with UE8M0 scales [E,2I,H/32] / [E,H,I/32] (uint8).
     """
     for name, t in (("hidden", hidden), ("topk_idx", topk_idx), ("topk_w", topk_w),
                     ("w_gate_up", w_gate_up), ("w_down", w_down)):

@@ -27,6 +27,9 @@ std::mutex g_devices_mu;
 // ---------------------------------------------------------------------------- validation
 
 bool is_fp8(const moe_problem& p) { return p.weight_dtype == MOE_FP8_E4M3; }
+bool is_fp4(const moe_problem& p) { return p.weight_dtype == MOE_FP4_E2M1; }
+// fp8 and fp4 experts take e4m3 activation rows with dynamic per-row scales
+bool quant_acts(const moe_problem& p) { return is_fp8(p) || is_fp4(p); }
 
 moe_status validate_problem(const moe_problem* p) {
   if (!p) return MOE_ERR_NULL_ARG;
@@ -34,7 +37,9 @@ moe_status validate_problem(const moe_problem* p) {
   const bool combo_bf16 = p->act_dtype == MOE_BF16 && p->weight_dtype == MOE_BF16 && p->scale_fmt == MOE_SCALE_NONE;
   const bool combo_fp8 = p->act_dtype == MOE_BF16 && p->weight_dtype == MOE_FP8_E4M3 &&
                          (p->scale_fmt == MOE_SCALE_F32 || p->scale_fmt == MOE_SCALE_UE8M0);
-  if (!(combo_f32 || combo_bf16 || combo_fp8)) return MOE_ERR_UNSUPPORTED;
+  const bool combo_fp4 = p->act_dtype == MOE_BF16 && p->weight_dtype == MOE_FP4_E2M1 &&
+                         p->scale_fmt == MOE_SCALE_UE8M0;
+  if (!(combo_f32 || combo_bf16 || combo_fp8 || combo_fp4)) return MOE_ERR_UNSUPPORTED;
   const uint32_t known = MOE_FLAG_CHECK_INDICES | MOE_FLAG_DETERMINISTIC | MOE_FLAG_FORCE_GROUPED |
                          MOE_FLAG_FORCE_DECODE | MOE_FLAG_ATOMIC_COMBINE | MOE_FLAG_ACT_GELU |
                          MOE_FLAG_ACT_RELU;
@@ -45,7 +50,7 @@ moe_status validate_problem(const moe_problem* p) {
   if (p->T < 0 || p->E < 1 || p->E > 1024 || p->k < 1 || p->k > p->E) return MOE_ERR_BAD_SHAPE;
   if (p->H <= 0 || p->I <= 0 || p->H > 65536 || p->I > 65536) return MOE_ERR_BAD_SHAPE;
   if (p->H % 128 != 0) return MOE_ERR_BAD_SHAPE;
-  if (p->I % (is_fp8(*p) ? 128 : 64) != 0) return MOE_ERR_BAD_SHAPE;
+  if (p->I % (quant_acts(*p) ? 128 : 64) != 0) return MOE_ERR_BAD_SHAPE;
   const int64_t A = p->T * (int64_t)p->k;
   if (A >= (int64_t(1) << 31)) return MOE_ERR_BAD_SHAPE;
   // work-item counts of the grouped kernels must fit in int32
@@ -107,6 +112,7 @@ Plan make_plan(const moe_problem& p) {
   if (!decode_capable(p)) decode = false;
   pl.path = decode ? kDecode : kGrouped;
   if (decode) pl.bm = decode_bm();
+  else if (is_fp4(p)) pl.bm = grouped_fp4_bm();
   else pl.bm = p.weight_dtype == MOE_F32 ? gateup_f32_bm() : (is_fp8(p) ? gateup_fp8_bm() : grouped_mfma_bm());
   pl.bm_dn = (!decode && is_fp8(p)) ? grouped_fp8_bm() : pl.bm;
   return pl;
@@ -118,9 +124,9 @@ struct Layout {
   size_t bad, counts, offsets, mt, mt_dn, perm, inv;
   size_t route_part; // chunked routing: per-chunk expert counts [G][E] and bad-id counts [G]
   size_t act;        // SwiGLU rows [A][I]: f32 (f32 weights, and fp8 before quantising) or bf16
-  size_t act_q;      // fp8: e4m3 SwiGLU rows [A][I]
-  size_t act_s;      // fp8: their scales [A][I/128]
-  size_t x_q, x_s;   // fp8: e4m3 hidden rows [T][H] and scales [T][H/128]
+  size_t act_q;      // fp8 / fp4: e4m3 SwiGLU rows [A][I]
+  size_t act_s;      // fp8 / fp4: their scales [A][I/128]
+  size_t x_q, x_s;   // fp8 / fp4: e4m3 hidden rows [T][H] and scales [T][H/128]
   size_t acc, slots, total;
 };
 
@@ -143,7 +149,7 @@ Layout make_layout(const moe_problem& p) {
   L.perm = take(4 * A);
   L.inv = take(4 * A);
   L.route_part = take(4 * (E + 1) * (size_t)kRouteMaxChunks);
-  const bool fp8 = p.weight_dtype == MOE_FP8_E4M3;
+  const bool fp8 = quant_acts(p);
   L.act = take((p.weight_dtype == MOE_BF16 ? 2 : 4) * A * I);
   L.act_q = fp8 ? take(A * I) : o;
   L.act_s = fp8 ? take(4 * A * (I / 128)) : o;
@@ -239,12 +245,16 @@ moe_status moe_plan_describe(const moe_problem* p, char* buf, size_t len) {
   if (!buf || len == 0) return MOE_ERR_NULL_ARG;
   const Plan pl = make_plan(*p);
   const Layout L = make_layout(*p);
-  const char* wname = p->weight_dtype == MOE_F32 ? "f32" : (p->weight_dtype == MOE_BF16 ? "bf16" : "fp8_e4m3");
+  const char* wname = p->weight_dtype == MOE_F32    ? "f32"
+                      : p->weight_dtype == MOE_BF16 ? "bf16"
+                      : is_fp4(*p)                  ? "fp4_e2m1"
+                                                    : "fp8_e4m3";
   const char* sname = p->scale_fmt == MOE_SCALE_F32 ? "f32" : (p->scale_fmt == MOE_SCALE_UE8M0 ? "ue8m0" : "none");
   const char* kern = pl.path == kDecode ? "stream_weights_16tok_mfma16x16x32"
                      : p->weight_dtype == MOE_F32 ? "fma_64x64"
                      : p->weight_dtype == MOE_BF16 ? "mfma32x32x16_bf16_160x256_k64_lds_dma_ring3"
-                                                   : "gateup_mfma32x32x16_widened_e4m3_160x128_ring4+down_mfma16x16x128_e4m3_128x256_ring3";
+                     : is_fp4(*p) ? "mfma16x16x128_e4m3xe2m1_scaled_128x256_ring3"
+                                  : "gateup_mfma32x32x16_widened_e4m3_160x128_ring4+down_mfma16x16x128_e4m3_128x256_ring3";
   const char* gname = (p->flags & MOE_FLAG_ACT_GELU) ? "geglu" : ((p->flags & MOE_FLAG_ACT_RELU) ? "reglu" : "swiglu");
   snprintf(buf, len, "path=%s weights=%s scales=%s kernels=%s activation=%s combine=%s workspace_bytes=%zu",
            pl.path == kDecode ? "decode" : "grouped", wname, sname, kern, gname,
@@ -336,7 +346,8 @@ moe_status moe_experts_forward(const moe_problem* p, const void* hidden, const i
   if (st != MOE_OK) return st;
   if (p->T == 0) return MOE_OK;
   if (!hidden || !topk_idx || !topk_w || !w_gate_up || !w_down || !out || !workspace) return MOE_ERR_NULL_ARG;
-  const bool fp8 = is_fp8(*p);
+  const bool fp8 = quant_acts(*p);     // e4m3 activation rows (fp8 and fp4 weights)
+  const bool fp4 = is_fp4(*p);
   if (fp8 && (!w_gate_up_scale || !w_down_scale)) return MOE_ERR_NULL_ARG;
   if (!aligned16(hidden) || !aligned16(w_gate_up) || !aligned16(w_down) || !aligned16(out) ||
       !aligned16(workspace) || !aligned4(topk_idx) || !aligned4(topk_w) || !aligned4(w_gate_up_scale) ||
@@ -423,7 +434,7 @@ moe_status moe_experts_forward(const moe_problem* p, const void* hidden, const i
   gu.b = w_gate_up;
   gu.b_scale = w_gate_up_scale;
   gu.b_rows = 2 * p->I;
-  gu.b_expert_stride = 2 * (int64_t)p->I * p->H;
+  gu.b_expert_stride = 2 * (int64_t)p->I * p->H / (fp4 ? 2 : 1);   // (fp4: bytes)
   gu.K = p->H;
   gu.act_out = ws + L.act;
   if (zero_in_gateup) {
@@ -440,7 +451,7 @@ moe_status moe_experts_forward(const moe_problem* p, const void* hidden, const i
   dn.b = w_down;
   dn.b_scale = w_down_scale;
   dn.b_rows = p->H;
-  dn.b_expert_stride = (int64_t)p->H * p->I;
+  dn.b_expert_stride = (int64_t)p->H * p->I / (fp4 ? 2 : 1);
   dn.K = p->I;
   dn.mt = mt_dn;
 
@@ -471,13 +482,14 @@ moe_status moe_experts_forward(const moe_problem* p, const void* hidden, const i
     MOE_HIP_CHECK(launch_down_f32(dn, max_mtiles(A, p->E, pl.bm) * dn.NT, s));
     MOE_HIP_CHECK(stage_mark(MOE_STAGE_DOWN, 1, s));
   } else {
-    const int gu_cols = fp8 ? gateup_fp8_cols() : gateup_bf16_cols();
-    const int dn_cols = fp8 ? down_fp8_cols() : down_bf16_cols();
+    const int gu_cols = fp4 ? gateup_fp4_cols() : (fp8 ? gateup_fp8_cols() : gateup_bf16_cols());
+    const int dn_cols = fp4 ? down_fp4_cols() : (fp8 ? down_fp8_cols() : down_bf16_cols());
     gu.NT = (p->I + gu_cols - 1) / gu_cols;
     dn.NT = (p->H + dn_cols - 1) / dn_cols;
     MOE_HIP_CHECK(stage_mark(MOE_STAGE_GATE_UP, 0, s));
     const int gu_grid = persistent_grid(dev->cus, 1, max_mtiles(A, p->E, pl.bm) * gu.NT);
-    MOE_HIP_CHECK(fp8 ? launch_gateup_fp8(gu, gu_grid, s) : launch_gateup_bf16(gu, gu_grid, s));
+    MOE_HIP_CHECK(fp4 ? launch_gateup_fp4(gu, gu_grid, s)
+                      : (fp8 ? launch_gateup_fp8(gu, gu_grid, s) : launch_gateup_bf16(gu, gu_grid, s)));
     MOE_HIP_CHECK(stage_mark(MOE_STAGE_GATE_UP, 1, s));
     if (fp8) {
       MOE_HIP_CHECK(stage_mark(MOE_STAGE_QUANT_ACT, 0, s));
@@ -488,7 +500,8 @@ moe_status moe_experts_forward(const moe_problem* p, const void* hidden, const i
     }
     MOE_HIP_CHECK(stage_mark(MOE_STAGE_DOWN, 0, s));
     const int dn_grid = persistent_grid(dev->cus, 1, max_mtiles(A, p->E, pl.bm_dn) * dn.NT);
-    MOE_HIP_CHECK(fp8 ? launch_down_fp8(dn, dn_grid, s) : launch_down_bf16(dn, dn_grid, s));
+    MOE_HIP_CHECK(fp4 ? launch_down_fp4(dn, dn_grid, s)
+                      : (fp8 ? launch_down_fp8(dn, dn_grid, s) : launch_down_bf16(dn, dn_grid, s)));
     MOE_HIP_CHECK(stage_mark(MOE_STAGE_DOWN, 1, s));
   }
 

@@ -90,6 +90,18 @@ __device__ __forceinline__ f32x4 mfma_16x16x128_e4m3(i32x8 a, i32x8 b, f32x4 c) 
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
+// C[16x16] = A[16x128] * B[128x16], A in e4m3 (32 bytes per lane, unit scale) and B in
+// e2m1 (16 bytes per lane).  With g = l >> 4, lane l holds B column (l & 15) and k 32 g ..
+// 32 g + 31 in nibble order (element 2j in the low nibble of byte j), and A row (l & 15)
+// with k 16 g .. 16 g + 15 in its first 16 bytes and k 64 + 16 g .. 64 + 16 g + 15 in its
+// last 16 (measured on gfx950 by one-hot operands; the two formats split k differently).
+// B is scaled per 32-k block by 2^(s - 127), s = the low byte of `scale_b` of the lane
+// holding that column and block.
+__device__ __forceinline__ f32x4 mfma_16x16x128_e4m3_e2m1(i32x8 a, i32x4 b, int scale_b) {
+  const i32x8 b8 = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};   // (only the low four are read)
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b8, f32x4{}, 0, 4, 0, 127, 0, scale_b);
+}
+
 // C[32x32] += A[32x64] * B[64x32] with e4m3 operands (32 bytes per lane: lane l holds
 // A row / B column (l & 31) and 32 k of group (l >> 5)), unit block scales.
 __device__ __forceinline__ f32x16 mfma_32x32x64_e4m3(i32x8 a, i32x8 b, f32x16 c) {

@@ -98,6 +98,14 @@ int down_fp8_cols();
 hipError_t launch_gateup_fp8(const GroupedArgs& g, int grid, hipStream_t s);
 hipError_t launch_down_fp8(const GroupedArgs& g, int grid, hipStream_t s);
 
+// e2m1 (FP4, 1x32 UE8M0 scales) x e4m3-row MFMA grouped GEMMs (persistent grid); B is
+// packed [E][b_rows][K/2] bytes (b_expert_stride in bytes), b_scale [E][b_rows][K/32]
+int grouped_fp4_bm();             // tile height of both fp4 GEMMs
+int gateup_fp4_cols();
+int down_fp4_cols();
+hipError_t launch_gateup_fp4(const GroupedArgs& g, int grid, hipStream_t s);
+hipError_t launch_down_fp4(const GroupedArgs& g, int grid, hipStream_t s);
+
 int gateup_f32_bm();
 int down_f32_bm();
 hipError_t launch_gateup_f32(const GroupedArgs& g, int64_t max_items, hipStream_t s);

@@ -48,6 +48,12 @@ def _ws(p):
     (dict(act=m.BF16, weight=m.BF16), m.OK),
     (dict(act=m.BF16, weight=m.FP8_E4M3, scale=m.SCALE_F32), m.OK),
     (dict(act=m.BF16, weight=m.FP8_E4M3, scale=m.SCALE_UE8M0), m.OK),
+    (dict(act=m.BF16, weight=m.FP4_E2M1, scale=m.SCALE_UE8M0), m.OK),
+    (dict(act=m.BF16, weight=m.FP4_E2M1, scale=m.SCALE_F32), m.ERR_UNSUPPORTED),   # fp4: UE8M0 only
+    (dict(act=m.BF16, weight=m.FP4_E2M1), m.ERR_UNSUPPORTED),
+    (dict(act=m.F32, weight=m.FP4_E2M1, scale=m.SCALE_UE8M0), m.ERR_UNSUPPORTED),
+    (dict(act=m.BF16, weight=m.FP4_E2M1, scale=m.SCALE_UE8M0, I=192), m.ERR_BAD_SHAPE),
+    (dict(act=m.BF16, weight=4, scale=m.SCALE_UE8M0), m.ERR_UNSUPPORTED),
     (dict(T=0), m.OK),
     (dict(k=9), m.ERR_BAD_SHAPE),
     (dict(k=0), m.ERR_BAD_SHAPE),
@@ -118,6 +124,15 @@ def test_forward_rejects_before_any_hip_call():
     st = L.moe_experts_forward(ctypes.byref(p8), fake, fake, fake, fake, fake, None, None, fake,
                                fake, 1 << 40, None)
     assert st == m.ERR_NULL_ARG
+    # fp4 without scale pointers; fp4 has no decode path
+    p4 = P(act=m.BF16, weight=m.FP4_E2M1, scale=m.SCALE_UE8M0)
+    st = L.moe_experts_forward(ctypes.byref(p4), fake, fake, fake, fake, fake, None, None, fake,
+                               fake, 1 << 40, None)
+    assert st == m.ERR_NULL_ARG
+    p4.flags = m.FLAG_FORCE_DECODE
+    st = L.moe_experts_forward(ctypes.byref(p4), fake, fake, fake, fake, fake, fake, fake, fake,
+                               fake, 1 << 40, None)
+    assert st == m.ERR_UNSUPPORTED
     # null problem
     assert L.moe_experts_forward(None, fake, fake, fake, fake, fake, None, None, fake, fake,
                                  1 << 40, None) == m.ERR_NULL_ARG
@@ -144,6 +159,25 @@ def test_plan_describe():
     s = m.plan_describe(P(act=m.BF16, weight=m.BF16, T=16, H=2048, I=1408, E=60, k=4,
                           flags=m.FLAG_FORCE_GROUPED))
     assert "path=grouped" in s
+    s = m.plan_describe(P(act=m.BF16, weight=m.FP4_E2M1, scale=m.SCALE_UE8M0, T=16, H=7168, I=2048,
+                          E=256, k=8))
+    assert "path=grouped" in s and "weights=fp4_e2m1" in s and "scales=ue8m0" in s
+
+
+def test_python_problem_infers_fp4_from_packed_shape():
+    import torch
+    x = torch.zeros(4, 256, dtype=torch.bfloat16)
+    idx = torch.zeros(4, 2, dtype=torch.int32)
+    gu4 = torch.zeros(3, 256, 128, dtype=torch.uint8)
+    dn4 = torch.zeros(3, 256, 64, dtype=torch.uint8)
+    p = m.problem_for(x, idx, gu4, dn4, torch.zeros(3, 256, 8, dtype=torch.uint8))
+    assert (p.weight_dtype, p.scale_fmt, p.I) == (m.FP4_E2M1, m.SCALE_UE8M0, 128)
+    gu8 = torch.zeros(3, 256, 256, dtype=torch.uint8)
+    dn8 = torch.zeros(3, 256, 128, dtype=torch.uint8)
+    p = m.problem_for(x, idx, gu8, dn8, torch.zeros(3, 2, 2, dtype=torch.float32))
+    assert (p.weight_dtype, p.scale_fmt, p.I) == (m.FP8_E4M3, m.SCALE_F32, 128)
+    with pytest.raises(ValueError):
+        m.problem_for(x, idx, gu4, dn4, None)
 
 
 def test_python_wrapper_rejects_cpu_tensors():

@@ -1,7 +1,9 @@
 """GPU experts forward vs the fp64 oracle, per element, within the stated tolerance.
 
-fp32 layers: |gpu - oracle| <= 1e-4 + 1e-4 |oracle|; bf16 (and fp8) layers:
-|gpu - oracle| <= 2e-2 + 2e-2 |oracle|.  Unselected experts are NaN-poisoned in
+fp32 layers: |gpu - oracle| <= 1e-4 + 1e-4 |oracle|; bf16 (and fp8, fp4) layers:
+|gpu - oracle| <= 2e-2 + 2e-2 |oracle|, plus, for fp8 and fp4, the effect of one e4m3 code
+step on every requantised SwiGLU element that lies within 3e-5 of a rounding midpoint
+(moe_helpers.requant_allowance).  Unselected experts are NaN-poisoned in
 every layer staged by synth.device_layer, so any read of them shows up as NaN.
 """
 
@@ -13,7 +15,7 @@ import mixture_experts_routed_topk_amd as m
 import synth
 from synth.device import device_layer
 from moe_helpers import (assert_close, gpu_out_f64, oracle_out, oracle_weights, prefetched_weights,
-                         sample_tokens)
+                         requant_allowance, sample_tokens)
 
 pytestmark = pytest.mark.gpu
 
@@ -42,7 +44,10 @@ def _full_check(spec, flags, tokens=None, what=""):
     ref = oracle_out(spec, D["x_host"], D["idx_host"], D["w_host"], W, tokens=tokens, gate=gate)
     got = out if tokens is None else out[tokens]
     print(f"{what or spec.name} flags={flags}: T={spec.T} active={len(D['active'])}")
-    return assert_close(got, ref, spec.act, what or spec.name)
+    extra = None
+    if spec.weight in ("fp8", "fp4"):
+        extra = requant_allowance(spec, D["x_host"], D["idx_host"], D["w_host"], W, tokens=tokens, gate=gate)
+    return assert_close(got, ref, spec.act, what or spec.name, extra)
 
 
 @pytest.mark.parametrize("path", list(PATHS))
@@ -185,6 +190,35 @@ def test_dsv3_fp8_sampled(name):
     _full_check(spec, 0, tokens=sample_tokens(spec.T, 24))
 
 
+# ----------------------------------------------------------------------------- fp4 experts
+
+@pytest.mark.parametrize("shape", [
+    dict(T=300, H=256, I=256, E=7, k=3),      # several M tiles, ragged tails
+    dict(T=1, H=128, I=128, E=4, k=2),
+    dict(T=200, H=384, I=128, E=64, k=2),     # many empty experts, a half N tile in down
+    dict(T=40, H=128, I=256, E=3, k=3),       # k == E
+    dict(T=129, H=512, I=384, E=5, k=2),
+    dict(T=37, H=256, I=128, E=1, k=1),       # a single expert
+])
+@pytest.mark.parametrize("flags", [0, m.FLAG_ATOMIC_COMBINE, m.FLAG_DETERMINISTIC])
+def test_small_fp4(shape, flags):
+    spec = synth.Spec("small_fp4", act="bf16", weight="fp4", scale="ue8m0", renorm=True, seed=23, **shape)
+    _full_check(spec, flags)
+
+
+def test_fp4_plan():
+    spec = synth.Spec("plan_fp4", T=16, H=256, I=128, E=4, k=2, act="bf16", weight="fp4", scale="ue8m0")
+    D = device_layer(spec)
+    prob = m.problem_for(D["x"], D["idx"], D["w_gate_up"], D["w_down"], D["w_gate_up_scale"])
+    assert prob.weight_dtype == m.FP4_E2M1
+    assert "weights=fp4_e2m1" in m.plan_describe(prob)
+
+
+def test_dsv3_fp4_sampled():
+    spec = synth.spec_for("dsv3_fp4_ue8m0")
+    _full_check(spec, 0, tokens=sample_tokens(spec.T, 24))
+
+
 def test_dsv3_bf16_sampled():
     spec = synth.spec_for("dsv3_prefill_bf16")
     _full_check(spec, 0, tokens=sample_tokens(spec.T, 24))
@@ -226,6 +260,7 @@ GATED_CASES = {
     "bf16_decode": (dict(T=40, H=256, I=256, E=6, k=2, act="bf16", weight="bf16"), m.FLAG_FORCE_DECODE),
     "f32": (dict(T=200, H=128, I=64, E=5, k=2, act="f32", weight="f32"), m.FLAG_FORCE_GROUPED),
     "fp8": (dict(T=200, H=256, I=256, E=5, k=2, act="bf16", weight="fp8", scale="f32"), 0),
+    "fp4": (dict(T=200, H=256, I=256, E=5, k=2, act="bf16", weight="fp4", scale="ue8m0"), 0),
 }
 
 
@@ -244,21 +279,21 @@ def test_gated_activations(gate, case):
 
 # ----------------------------------------------------------------------------- limits
 
-@pytest.mark.parametrize("weight", ["bf16", "fp8"])
+@pytest.mark.parametrize("weight", ["bf16", "fp8", "fp4"])
 def test_max_experts(weight):
     # E at the library's maximum (1024): most experts empty, 16-bit M-tile tables in LDS
     shape = dict(T=700, H=256, I=128, E=1024, k=8) if weight == "bf16" else dict(T=300, H=256, I=128, E=1024, k=4)
-    extra = dict(scale="ue8m0") if weight == "fp8" else {}
+    extra = dict(scale="ue8m0") if weight != "bf16" else {}
     spec = synth.Spec(f"maxE_{weight}", act="bf16", weight=weight, renorm=True, seed=17, **shape, **extra)
     _full_check(spec, m.FLAG_FORCE_GROUPED | m.FLAG_ATOMIC_COMBINE)
     _full_check(spec, m.FLAG_FORCE_GROUPED)
 
 
-@pytest.mark.parametrize("weight", ["bf16", "fp8"])
+@pytest.mark.parametrize("weight", ["bf16", "fp8", "fp4"])
 def test_wide_hidden(weight):
     # a long K loop in gate_up (H = 16384: 256 bf16 slices / 128 e4m3 scale blocks) and
     # 64 output tiles in down
-    extra = dict(scale="f32") if weight == "fp8" else {}
+    extra = {"bf16": {}, "fp8": dict(scale="f32"), "fp4": dict(scale="ue8m0")}[weight]
     spec = synth.Spec(f"wideH_{weight}", T=96, H=16384, I=128, E=4, k=2, act="bf16", weight=weight,
                       renorm=True, seed=19, **extra)
     _full_check(spec, m.FLAG_FORCE_GROUPED)
