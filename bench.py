@@ -26,7 +26,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0                                            # MI355X HBM3E, GB/s
-PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}      # dense, TFLOP/s
+# dense, TFLOP/s; the fp4 experts multiply e4m3 activations by e2m1 weights, a mixed-format
+# MFMA that issues at the fp8 rate (the 10.1 PFLOP/s fp4 figure needs 4-bit operands on both
+# sides), so they are priced at the fp8 peak
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 5000.0, "f32": 157.3}
 
 WORKLOADS = {
     "tiny_fp32": "tiny fp32 MoE layer: T=32 H=128 I=256 E=8 top-2, renormalised",
@@ -35,6 +38,7 @@ WORKLOADS = {
     "dsv3_prefill_bf16": "DeepSeek-V3-shaped bf16 prefill, Zipf-skewed routing: T=8192 H=7168 I=2048 E=256 top-8",
     "dsv3_fp8_f32scale": "DeepSeek-V3-shaped fp8-e4m3 experts, 128x128 float32 block scales: T=4096 H=7168 I=2048 E=256 top-8",
     "dsv3_fp8_ue8m0": "DeepSeek-V3-shaped fp8-e4m3 experts, 128x128 UE8M0 block scales: T=4096 H=7168 I=2048 E=256 top-8",
+    "dsv3_fp4_ue8m0": "DeepSeek-V3-shaped fp4-e2m1 experts (two per byte), 1x32 UE8M0 scales: T=4096 H=7168 I=2048 E=256 top-8",
 }
 
 
@@ -114,23 +118,27 @@ def router_step(spec, dev, iters=50):
 def algorithmic(spec, active_count, stage):
     """(flops, bytes) the method must do/move in one launch of a stage."""
     A, H, I = spec.A, spec.H, spec.I
-    wb = {"f32": 4, "bf16": 2, "fp8": 1}[spec.weight]
+    wb = {"f32": 4, "bf16": 2, "fp8": 1, "fp4": 0.5}[spec.weight]
     xb = {"f32": 4, "bf16": 2}[spec.act]
-    ab = {"f32": 4, "bf16": 2, "fp8": 1}[spec.weight]          # SwiGLU rows as stored
-    sb = 0
+    ab = {"f32": 4, "bf16": 2, "fp8": 1, "fp4": 1}[spec.weight]   # SwiGLU rows as stored
+    q = spec.weight in ("fp8", "fp4")                               # e4m3 activation rows
+    # weight-scale bytes per weight element: 128x128 blocks (fp8) or 1x32 UE8M0 (fp4)
+    sb = 0.0
     if spec.weight == "fp8":
-        sb = 4 if spec.scale == "f32" else 1
+        sb = (4 if spec.scale == "f32" else 1) / (128 * 128)
+    elif spec.weight == "fp4":
+        sb = 1 / 32
     if stage == "gate_up":
         flops = 4.0 * A * H * I
-        byts = active_count * (2 * I * H * wb + (2 * I // 128) * (H // 128) * sb)
-        byts += spec.T * H * (1 if spec.weight == "fp8" else xb) + A * I * ab
-        if spec.weight == "fp8":
+        byts = active_count * 2 * I * H * (wb + sb)
+        byts += spec.T * H * (1 if q else xb) + A * I * ab
+        if q:
             byts += spec.T * (H // 128) * 4 + A * (I // 128) * 4
     elif stage == "down":
         flops = 2.0 * A * H * I
-        byts = active_count * (H * I * wb + (H // 128) * (I // 128) * sb)
+        byts = active_count * H * I * (wb + sb)
         byts += A * I * ab + spec.T * H * 4
-        if spec.weight == "fp8":
+        if q:
             byts += A * (I // 128) * 4
     else:
         raise ValueError(stage)
@@ -139,21 +147,25 @@ def algorithmic(spec, active_count, stage):
 
 def layer_totals(spec, active_count):
     """Whole-layer algorithmic flops and bytes (active expert weights + x + out + routing)."""
-    wb = {"f32": 4, "bf16": 2, "fp8": 1}[spec.weight]
+    wb = {"f32": 4, "bf16": 2, "fp8": 1, "fp4": 0.5}[spec.weight]
     xb = {"f32": 4, "bf16": 2}[spec.act]
     flops = 6.0 * spec.A * spec.H * spec.I
     byts = active_count * 3 * spec.I * spec.H * wb + 2 * spec.T * spec.H * xb + 8 * spec.A
     if spec.weight == "fp8":
         sb = 4 if spec.scale == "f32" else 1
         byts += active_count * 3 * (spec.I // 128) * (spec.H // 128) * sb
+    elif spec.weight == "fp4":
+        byts += active_count * 3 * spec.I * spec.H / 32
     return flops, float(byts)
 
 
 KERNEL_SOURCES = {   # (path, weight dtype, stage) -> kernel source files, for the traffic record
     ("grouped", "bf16", "gate_up"): ["grouped_bf16.hip"],
     ("grouped", "bf16", "down"): ["grouped_bf16.hip"],
-    ("grouped", "fp8", "gate_up"): ["grouped_fp8_gateup.hip"],
-    ("grouped", "fp8", "down"): ["grouped_fp8_down.hip"],
+    ("grouped", "fp8", "gate_up"): ["grouped_fp8.hip"],
+    ("grouped", "fp8", "down"): ["grouped_fp8.hip"],
+    ("grouped", "fp4", "gate_up"): ["grouped_fp4.hip"],
+    ("grouped", "fp4", "down"): ["grouped_fp4.hip"],
     ("grouped", "f32", "gate_up"): ["grouped_f32.hip"],
     ("grouped", "f32", "down"): ["grouped_f32.hip"],
     ("decode", "bf16", "gate_up"): ["decode.hip"],
@@ -218,8 +230,8 @@ def cpu_baseline(spec, D, seconds: float):
             cache[key] = (synth.expert_gate_up if which == 0 else synth.expert_down)(spec, e)
         return cache[key]
 
-    if spec.weight == "fp8":
-        W = ExpertWeights("fp8", lambda e: get(0, e)[0], lambda e: get(1, e)[0], spec.scale,
+    if spec.weight in ("fp8", "fp4"):
+        W = ExpertWeights(spec.weight, lambda e: get(0, e)[0], lambda e: get(1, e)[0], spec.scale,
                           lambda e: get(0, e)[1], lambda e: get(1, e)[1])
     else:
         W = ExpertWeights(spec.weight, lambda e: get(0, e), lambda e: get(1, e))
@@ -279,7 +291,7 @@ def main():
     D = device_layer(spec, dev)
     n_active = len(D["active"])
     kw = {}
-    if spec.weight == "fp8":
+    if spec.weight in ("fp8", "fp4"):
         kw = dict(w_gate_up_scale=D["w_gate_up_scale"], w_down_scale=D["w_down_scale"])
     prob = m.problem_for(D["x"], D["idx"], D["w_gate_up"], D["w_down"], kw.get("w_gate_up_scale"),
                          args.flags)

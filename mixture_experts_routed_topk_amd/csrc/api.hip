@@ -113,8 +113,8 @@ Plan make_plan(const moe_problem& p) {
   pl.path = decode ? kDecode : kGrouped;
   if (decode) pl.bm = decode_bm();
   else if (is_fp4(p)) pl.bm = grouped_fp4_bm();
-  else pl.bm = p.weight_dtype == MOE_F32 ? gateup_f32_bm() : (is_fp8(p) ? gateup_fp8_bm() : grouped_mfma_bm());
-  pl.bm_dn = (!decode && is_fp8(p)) ? grouped_fp8_bm() : pl.bm;
+  else pl.bm = p.weight_dtype == MOE_F32 ? gateup_f32_bm() : (is_fp8(p) ? grouped_fp8_bm() : grouped_mfma_bm());
+  pl.bm_dn = pl.bm;
   return pl;
 }
 
@@ -254,7 +254,7 @@ moe_status moe_plan_describe(const moe_problem* p, char* buf, size_t len) {
                      : p->weight_dtype == MOE_F32 ? "fma_64x64"
                      : p->weight_dtype == MOE_BF16 ? "mfma32x32x16_bf16_160x256_k64_lds_dma_ring3"
                      : is_fp4(*p) ? "mfma16x16x128_e4m3xe2m1_scaled_128x256_ring3"
-                                  : "gateup_mfma32x32x16_widened_e4m3_160x128_ring4+down_mfma16x16x128_e4m3_128x256_ring3";
+                                  : "mfma16x16x128_e4m3_scaled_128x256_ring3";
   const char* gname = (p->flags & MOE_FLAG_ACT_GELU) ? "geglu" : ((p->flags & MOE_FLAG_ACT_RELU) ? "reglu" : "swiglu");
   snprintf(buf, len, "path=%s weights=%s scales=%s kernels=%s activation=%s combine=%s workspace_bytes=%zu",
            pl.path == kDecode ? "decode" : "grouped", wname, sname, kern, gname,

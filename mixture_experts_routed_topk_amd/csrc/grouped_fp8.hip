@@ -1,18 +1,26 @@
-// e4m3 down-projection grouped GEMM + routing weight + combine on MFMA (gfx950).
+// e4m3 grouped GEMMs of the expert MLP on MFMA (gfx950): gate_up + SwiGLU, and down +
+// routing weight + combine.
 //
 // The "FP8 and FP4 quantized experts" section of the Experts backends page (and its
-// note): e4m3 weights W_down[e] ([H, I], K = I contiguous) with 128x128 block scales
-// (float32 or UE8M0, used directly) and the e4m3 SwiGLU rows with dynamic per-row
-// scales over 128-column blocks.  Output column n of sorted row m is
+// note): e4m3 weights ([2I, H] gate_up, [H, I] down; K contiguous) with 128x128 block
+// scales (float32 or UE8M0, used directly) and e4m3 activation rows (the hidden states,
+// then the SwiGLU rows) with dynamic per-row scales over 128-column blocks.  For sorted
+// row m and weight row n
 //     y[m, n] = sum over 128-blocks kb of  sa[m, kb] * sw[n, kb] * sum_{k in kb} a[m, k] w[n, k]
 // The inner sum of one block is one 16x16x128 e4m3 MFMA; its result is folded into the
-// float32 accumulator times the two scales.  The epilogue multiplies by the routing
-// weight and adds the row into the token's float32 output row (hardware float atomics)
-// or stores it to the slot's own row (per-slot combine).
+// float32 accumulator times the two scales.
 //
-// Tiles of up to 128 rows x 256 output columns; eight waves in a 2 x 4 grid, wave
-// (wm, wn) owning the 16-row fragments wm, wm + 2, .., wm + 6 and output columns
-// 64 wn .. 64 wn + 63 (four 16-column fragments).  K advances in slices of 128 codes (one
+// gate_up: a tile's 256 weight rows are 128 gate rows and the matching 128 up rows, so the
+// epilogue forms gate(g) * u for 128 SwiGLU columns in registers and writes it as float32
+// (requantised to e4m3 by the row quantiser before the down projection).  down: 256 output
+// columns; the epilogue multiplies by the routing weight and adds the row into the token's
+// float32 output row (hardware float atomics) or stores it to the slot's own row
+// (per-slot combine).
+//
+// Tiles of up to 128 rows x 256 weight rows; eight waves in a 2 x 4 grid, wave (wm, wn)
+// owning the 16-row fragments wm, wm + 2, .., wm + 6 and four 16-column fragments (down:
+// columns 64 wn .. 64 wn + 63; gate_up: gate columns 32 wn .. 32 wn + 31 and the matching
+// up columns).  K advances in slices of 128 codes (one
 // scale block) held in a three-slot LDS ring filled by global->LDS DMA: slices kt + 1
 // and kt + 2 stream in while slice kt is multiplied, the DMA of kt + 2 spread over the
 // slice's work.  Slot rows are 128 bytes with 16-byte chunks XOR-permuted by
@@ -45,7 +53,7 @@ constexpr int kMaxE = 1024;
 constexpr int kMaxKB = 512;                // K / 128 (K = I <= 65536)
 static_assert(ALD <= 4 && BLD == 4, "the DMA of a slice is spread over four parts");
 
-enum { kDownAtomic = 1, kDownSlots = 2 };
+enum { kGateUp = 0, kDownAtomic = 1, kDownSlots = 2 };
 
 __device__ __forceinline__ int chunk_slot(int row, int c) { return c ^ ((row >> 1) & 7); }
 
@@ -56,7 +64,7 @@ __device__ __forceinline__ float ue8m0_value(uint32_t b) {
 }
 
 template <int MODE>
-__global__ __launch_bounds__(kThreads, 1) void grouped_fp8_down_kernel(GroupedArgs g) {
+__global__ __launch_bounds__(kThreads, 1) void grouped_fp8_kernel(GroupedArgs g) {
   __shared__ __attribute__((aligned(1024))) char ring[NSTAGE][STAGE];
   __shared__ float sSb[2][kMaxKB];          // the item's weight block scales (two row blocks)
   __shared__ uint16_t sMt[kMaxE + 1];
@@ -75,6 +83,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_fp8_down_kernel(GroupedAr
   const char* __restrict__ Sbase = reinterpret_cast<const char*>(g.a_scale);
   const uint32_t a_row_bytes = (uint32_t)g.lda;
   const uint32_t b_row_bytes = (uint32_t)g.K;
+  const int ncols = MODE == kGateUp ? g.I : g.H;     // output columns of the whole GEMM
 
   const int n_mt = g.mt[E];
   const bool mt_lds = n_mt < 65536;
@@ -90,6 +99,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_fp8_down_kernel(GroupedAr
   // slice: logical chunks 2 g4 and 2 g4 + 1
   const uint32_t foff0 = (uint32_t)(l16 * ROWB + (chunk_slot(l16, 2 * g4) << 4));
   const uint32_t foff1 = (uint32_t)(l16 * ROWB + (chunk_slot(l16, 2 * g4 + 1) << 4));
+
+  // tile column (weight row) of fragment j of this wave: gate_up pairs gate fragment j
+  // with up fragment j + 2 (the same SwiGLU column)
+  auto bcol0 = [&](int j) __attribute__((always_inline)) -> int {
+    if (MODE == kGateUp) return j < 2 ? 32 * wn + 16 * j : BN / 2 + 32 * wn + 16 * (j - 2);
+    return 64 * wn + 16 * j;
+  };
 
   f32x4 acc[MFRAG][NFRAG];
 
@@ -116,17 +132,28 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_fp8_down_kernel(GroupedAr
     if (rows <= 0) continue;
     const char* __restrict__ Bexp = static_cast<const char*>(g.b) + (int64_t)e * g.b_expert_stride;
 
-    auto b_row = [&](int c) __attribute__((always_inline)) -> int { return min(nt * BN + c, g.H - 1); };
-    auto a_src = [&](int r) __attribute__((always_inline)) -> int { return row0 + min(r, rows - 1); };
+    // weight row of tile column c (columns past the matrix repeat its last row)
+    auto b_row = [&](int c) __attribute__((always_inline)) -> int {
+      if (MODE == kGateUp) {
+        const int i = min(nt * (BN / 2) + (c % (BN / 2)), g.I - 1);
+        return c < BN / 2 ? i : g.I + i;
+      }
+      return min(nt * BN + c, g.H - 1);
+    };
+    auto a_src = [&](int r) __attribute__((always_inline)) -> int {   // (rows past the end repeat the last)
+      const int p = row0 + min(r, rows - 1);
+      return g.a_rows ? g.a_rows[p] / g.a_row_div : p;
+    };
 
-    // the item's weight block scales: row blocks of output columns nt*256 .. +127, +128 .. +255
+    // the item's weight block scales: the 128-row blocks of tile columns 0 .. 127 and
+    // 128 .. 255 (gate_up: the gate rows and the up rows of the tile)
     {
       const int KB = KT;
       const int64_t nblk_rows = g.b_rows / 128;
       for (int i = tid; i < 2 * KB; i += kThreads) {
         const int hb = i < KB ? 0 : 1;
         const int kb = i - hb * KB;
-        const int64_t blk = (int64_t)e * nblk_rows + min(nt * BN + 128 * hb, g.H - 1) / 128;
+        const int64_t blk = (int64_t)e * nblk_rows + b_row(128 * hb) / 128;
         float v;
         if (g.b_scale_ue8m0) v = ue8m0_value(static_cast<const uint8_t*>(g.b_scale)[blk * KB + kb]);
         else v = static_cast<const float*>(g.b_scale)[blk * KB + kb];
@@ -135,7 +162,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_fp8_down_kernel(GroupedAr
     }
     int my_tok = 0;
     float my_wt = 0.f;
-    if (tid < rows) {
+    if (MODE != kGateUp && tid < rows) {
       const int slot = g.perm[row0 + tid];
       my_tok = MODE == kDownAtomic ? slot / g.k : slot;
       my_wt = g.topk_w[slot];
@@ -193,11 +220,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_fp8_down_kernel(GroupedAr
       const char* As = &ring[slot][0];
       const char* Bs = As + BM * ROWB;
       const float* Sa = reinterpret_cast<const float*>(As + SA_OFF);
-      const float sb = sSb[wn >> 1][kt];   // the wave's 64 columns lie in one 128-row block
+      // weight block scale of fragment j: down, the wave's 64 columns lie in one 128-row
+      // block; gate_up, fragments 0, 1 are gate rows and 2, 3 the matching up rows
+      const float sb0 = sSb[MODE == kGateUp ? 0 : wn >> 1][kt];
+      const float sb1 = sSb[MODE == kGateUp ? 1 : wn >> 1][kt];
       i32x8 bf[NFRAG];
 #pragma unroll
       for (int j = 0; j < NFRAG; ++j) {
-        const char* bp = Bs + (wn * 64 + j * 16) * ROWB;
+        const char* bp = Bs + bcol0(j) * ROWB;
         const i32x4 lo = *reinterpret_cast<const i32x4*>(bp + foff0);
         const i32x4 hi = *reinterpret_cast<const i32x4*>(bp + foff1);
         bf[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -210,14 +240,17 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_fp8_down_kernel(GroupedAr
           const i32x4 hi = *reinterpret_cast<const i32x4*>(ap + foff1);
           const i32x8 af = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           const f32x4 sa = *reinterpret_cast<const f32x4*>(&Sa[(2 * i + wm) * 16 + 4 * g4]);
-          f32x4 s;
+          f32x4 s0, s1;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) s[q] = sa[q] * sb;
+          for (int q = 0; q < 4; ++q) {
+            s0[q] = sa[q] * sb0;
+            s1[q] = sa[q] * sb1;
+          }
 #pragma unroll
           for (int j = 0; j < NFRAG; ++j) {
             const f32x4 pr = mfma_16x16x128_e4m3(af, bf[j], f32x4{});
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc[i][j][q] = fmaf(pr[q], s[q], acc[i][j][q]);
+            for (int q = 0; q < 4; ++q) acc[i][j][q] = fmaf(pr[q], j < 2 ? s0[q] : s1[q], acc[i][j][q]);
           }
         }
         if (next) issue_part(kt + 2, nslot, i);
@@ -245,28 +278,47 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_fp8_down_kernel(GroupedAr
       default: kloop(std::integral_constant<int, 0>{}); break;
     }
 
-    if (tid < BM) {
-      sTok[tid] = my_tok;
-      sWt[tid] = my_wt;
-    }
-    __syncthreads();
-    // 16x16 fragment (i, j): element q at tile row (2 i + wm) * 16 + 4 g4 + q, column
-    // 64 wn + 16 j + l16
+    // 16x16 fragment (i, j): element q at tile row (2 i + wm) * 16 + 4 g4 + q, tile column
+    // bcol0(j) + l16
+    if constexpr (MODE == kGateUp) {
+      float* out = static_cast<float*>(g.act_out);
 #pragma unroll
-    for (int i = 0; i < MFRAG; ++i) {
-      if ((2 * i + wm) * 16 >= rows) break;
+      for (int i = 0; i < MFRAG; ++i) {
+        if ((2 * i + wm) * 16 >= rows) break;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r = (2 * i + wm) * 16 + 4 * g4 + q;
-        if (r >= rows) continue;
-        const float wt = sWt[r];
-        const int64_t tok = sTok[r];
+        for (int q = 0; q < 4; ++q) {
+          const int r = (2 * i + wm) * 16 + 4 * g4 + q;
+          if (r >= rows) continue;
 #pragma unroll
-        for (int j = 0; j < NFRAG; ++j) {
-          const int col = nt * BN + wn * 64 + j * 16 + l16;
-          if (col < g.H) {
-            if (MODE == kDownAtomic) unsafeAtomicAdd(g.acc_out + tok * g.H + col, wt * acc[i][j][q]);
-            else g.slot_out[tok * g.H + col] = wt * acc[i][j][q];
+          for (int j = 0; j < 2; ++j) {
+            const int col = nt * (BN / 2) + 32 * wn + 16 * j + l16;
+            if (col < ncols)
+              out[(int64_t)(row0 + r) * g.I + col] = gate_fn<false>(g.gate, acc[i][j][q]) * acc[i][j + 2][q];
+          }
+        }
+      }
+    } else {
+      if (tid < BM) {
+        sTok[tid] = my_tok;
+        sWt[tid] = my_wt;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < MFRAG; ++i) {
+        if ((2 * i + wm) * 16 >= rows) break;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = (2 * i + wm) * 16 + 4 * g4 + q;
+          if (r >= rows) continue;
+          const float wt = sWt[r];
+          const int64_t tok = sTok[r];
+#pragma unroll
+          for (int j = 0; j < NFRAG; ++j) {
+            const int col = nt * BN + bcol0(j) + l16;
+            if (col < ncols) {
+              if (MODE == kDownAtomic) unsafeAtomicAdd(g.acc_out + tok * g.H + col, wt * acc[i][j][q]);
+              else g.slot_out[tok * g.H + col] = wt * acc[i][j][q];
+            }
           }
         }
       }
@@ -278,14 +330,17 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_fp8_down_kernel(GroupedAr
 template <int MODE>
 hipError_t launch(const GroupedArgs& g, int grid, hipStream_t s) {
   if (g.K / ROWB > kMaxKB) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((grouped_fp8_down_kernel<MODE>), dim3(grid), dim3(kThreads), 0, s, g);
+  hipLaunchKernelGGL((grouped_fp8_kernel<MODE>), dim3(grid), dim3(kThreads), 0, s, g);
   return hipGetLastError();
 }
 
 }  // namespace
 
 int grouped_fp8_bm() { return BM; }
+int gateup_fp8_cols() { return BN / 2; }
 int down_fp8_cols() { return BN; }
+
+hipError_t launch_gateup_fp8(const GroupedArgs& g, int grid, hipStream_t s) { return launch<kGateUp>(g, grid, s); }
 
 hipError_t launch_down_fp8(const GroupedArgs& g, int grid, hipStream_t s) {
   return g.slot_out ? launch<kDownSlots>(g, grid, s) : launch<kDownAtomic>(g, grid, s);

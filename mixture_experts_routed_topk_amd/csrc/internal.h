@@ -91,8 +91,7 @@ hipError_t launch_gateup_bf16(const GroupedArgs& g, int grid, hipStream_t s);
 hipError_t launch_down_bf16(const GroupedArgs& g, int grid, hipStream_t s);
 
 // e4m3 (128x128 block-scaled) MFMA grouped GEMMs (persistent grid)
-int grouped_fp8_bm();             // tile height of the e4m3 down GEMM
-int gateup_fp8_bm();              // tile height of the e4m3 gate/up GEMM
+int grouped_fp8_bm();             // tile height of both e4m3 GEMMs
 int gateup_fp8_cols();
 int down_fp8_cols();
 hipError_t launch_gateup_fp8(const GroupedArgs& g, int grid, hipStream_t s);
