@@ -75,8 +75,7 @@ enum Path { kGrouped = 0, kDecode = 1 };
 
 struct Plan {
   Path path;
-  int bm;     // row-group height of the tile table the gate/up GEMM walks
-  int bm_dn;  // ... and the down GEMM (a second table when it differs)
+  int bm;     // row-group height of the M-tile table both GEMMs walk
 };
 
 // Combine by per-slot rows (each slot's weighted row stored, the k rows of a token summed
@@ -114,14 +113,13 @@ Plan make_plan(const moe_problem& p) {
   if (decode) pl.bm = decode_bm();
   else if (is_fp4(p)) pl.bm = grouped_fp4_bm();
   else pl.bm = p.weight_dtype == MOE_F32 ? gateup_f32_bm() : (is_fp8(p) ? grouped_fp8_bm() : grouped_mfma_bm());
-  pl.bm_dn = pl.bm;
   return pl;
 }
 
 // ---------------------------------------------------------------------------- workspace
 
 struct Layout {
-  size_t bad, counts, offsets, mt, mt_dn, perm, inv;
+  size_t bad, counts, offsets, mt, perm, inv;
   size_t route_part; // chunked routing: per-chunk expert counts [G][E] and bad-id counts [G]
   size_t act;        // SwiGLU rows [A][I]: f32 (f32 weights, and fp8 before quantising) or bf16
   size_t act_q;      // fp8 / fp4: e4m3 SwiGLU rows [A][I]
@@ -145,7 +143,6 @@ Layout make_layout(const moe_problem& p) {
   L.counts = take(4 * E);
   L.offsets = take(4 * (E + 1));
   L.mt = take(4 * (E + 1));
-  L.mt_dn = take(4 * (E + 1));
   L.perm = take(4 * A);
   L.inv = take(4 * A);
   L.route_part = take(4 * (E + 1) * (size_t)kRouteMaxChunks);
@@ -372,7 +369,6 @@ moe_status moe_experts_forward(const moe_problem* p, const void* hidden, const i
   int32_t* bad = reinterpret_cast<int32_t*>(ws + L.bad);
   int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
   int32_t* mt = reinterpret_cast<int32_t*>(ws + L.mt);
-  int32_t* mt_dn = pl.bm_dn != pl.bm ? reinterpret_cast<int32_t*>(ws + L.mt_dn) : mt;
   int32_t* perm = reinterpret_cast<int32_t*>(ws + L.perm);
   int32_t* inv = reinterpret_cast<int32_t*>(ws + L.inv);
   float* acc = det ? nullptr : reinterpret_cast<float*>(ws + L.acc);
@@ -400,10 +396,6 @@ moe_status moe_experts_forward(const moe_problem* p, const void* hidden, const i
   r.bad = bad;
   r.bm0 = pl.bm;
   r.mt0 = mt;
-  if (mt_dn != mt) {
-    r.bm1 = pl.bm_dn;
-    r.mt1 = mt_dn;
-  }
   r.part = reinterpret_cast<int32_t*>(ws + L.route_part);
   MOE_HIP_CHECK(stage_mark(MOE_STAGE_ROUTE, 0, s));
   MOE_HIP_CHECK(launch_route(r, s));
@@ -453,7 +445,6 @@ moe_status moe_experts_forward(const moe_problem* p, const void* hidden, const i
   dn.b_rows = p->H;
   dn.b_expert_stride = (int64_t)p->H * p->I / (fp4 ? 2 : 1);
   dn.K = p->I;
-  dn.mt = mt_dn;
 
   if (fp8) {
     MOE_HIP_CHECK(stage_mark(MOE_STAGE_QUANT_X, 0, s));
@@ -499,7 +490,7 @@ moe_status moe_experts_forward(const moe_problem* p, const void* hidden, const i
       MOE_HIP_CHECK(stage_mark(MOE_STAGE_QUANT_ACT, 1, s));
     }
     MOE_HIP_CHECK(stage_mark(MOE_STAGE_DOWN, 0, s));
-    const int dn_grid = persistent_grid(dev->cus, 1, max_mtiles(A, p->E, pl.bm_dn) * dn.NT);
+    const int dn_grid = persistent_grid(dev->cus, 1, max_mtiles(A, p->E, pl.bm) * dn.NT);
     MOE_HIP_CHECK(fp4 ? launch_down_fp4(dn, dn_grid, s)
                       : (fp8 ? launch_down_fp8(dn, dn_grid, s) : launch_down_bf16(dn, dn_grid, s)));
     MOE_HIP_CHECK(stage_mark(MOE_STAGE_DOWN, 1, s));

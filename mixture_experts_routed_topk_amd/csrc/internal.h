@@ -18,10 +18,8 @@ struct RouteArgs {
   int32_t* perm;       // [A]
   int32_t* inv;        // [A] (may be null)
   int32_t* bad;        // [1] out-of-range ids (may be null)
-  int bm0;             // tile height of table mt0 (0 = none)
+  int bm0;             // tile height of the M-tile table mt0 (0 = no table)
   int32_t* mt0;        // [E+1]
-  int bm1;
-  int32_t* mt1;
   // batches of more than kRouteOneBlockMax slots are routed in route_chunks(A) chunks of
   // route_chunk(A) slots; part holds (E + 1) * route_chunks(A) ints of scratch (when
   // null, one workgroup routes the whole batch)

@@ -186,11 +186,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs p) {
     if (p.bad) *p.bad = bad;
   }
 
-  // 3. M-tile starts for up to two tile heights: mt[e] = sum_{e' < e} ceil(count / bm)
-  for (int t = 0; t < 2; ++t) {
-    const int bm = t == 0 ? p.bm0 : p.bm1;
-    int32_t* mt = t == 0 ? p.mt0 : p.mt1;
-    if (bm <= 0 || mt == nullptr) continue;
+  // 3. M-tile starts of the grouped GEMMs' tile height: mt[e] = sum_{e' < e} ceil(count / bm)
+  //    (uniform condition: every thread takes the same branch)
+  if (p.bm0 > 0 && p.mt0 != nullptr) {
+    const int bm = p.bm0;
+    int32_t* mt = p.mt0;
     __syncthreads();
     for (int e = tid; e < E; e += kRouteThreads) {
       const int c = (e + 1 < E ? offs[e + 1] : valid) - offs[e];
@@ -345,21 +345,18 @@ __global__ __launch_bounds__(kRouteThreads) void route_place_kernel(RouteArgs p)
   }
   __syncthreads();
 
-  if (g == 0) {   // M-tile starts for up to two tile heights
-    for (int t = 0; t < 2; ++t) {
-      const int bm = t == 0 ? p.bm0 : p.bm1;
-      int32_t* mt = t == 0 ? p.mt0 : p.mt1;
-      if (bm <= 0 || mt == nullptr) continue;
-      __syncthreads();
-      for (int e = tid; e < E; e += kRouteThreads) {
-        const int c = (e + 1 < E ? offs[e + 1] : valid) - offs[e];
-        tiles[e] = c == 0 ? 0 : (c - 1) / bm + 1;
-      }
-      __syncthreads();
-      const int nt = block_exclusive_scan(tiles, E, wave_sums);
-      for (int e = tid; e < E; e += kRouteThreads) mt[e] = tiles[e];
-      if (tid == 0) mt[E] = nt;
+  if (g == 0 && p.bm0 > 0 && p.mt0 != nullptr) {   // M-tile starts of the grouped GEMMs
+    const int bm = p.bm0;
+    int32_t* mt = p.mt0;
+    __syncthreads();
+    for (int e = tid; e < E; e += kRouteThreads) {
+      const int c = (e + 1 < E ? offs[e + 1] : valid) - offs[e];
+      tiles[e] = c == 0 ? 0 : (c - 1) / bm + 1;
     }
+    __syncthreads();
+    const int nt = block_exclusive_scan(tiles, E, wave_sums);
+    for (int e = tid; e < E; e += kRouteThreads) mt[e] = tiles[e];
+    if (tid == 0) mt[E] = nt;
     __syncthreads();
   }
 
