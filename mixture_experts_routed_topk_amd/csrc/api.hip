@@ -101,7 +101,9 @@ bool slot_rows_bf16(const moe_problem& p, bool decode) {
          p.act_dtype == MOE_BF16;
 }
 
-bool decode_capable(const moe_problem& p) { return p.weight_dtype == MOE_BF16 && p.I % 128 == 0; }
+bool decode_capable(const moe_problem& p) {
+  return p.weight_dtype == MOE_BF16 && p.I % 128 == 0 && p.T * p.k <= kDecodeMaxSlots;
+}
 
 Plan make_plan(const moe_problem& p) {
   Plan pl;
@@ -247,7 +249,7 @@ moe_status moe_plan_describe(const moe_problem* p, char* buf, size_t len) {
                       : is_fp4(*p)                  ? "fp4_e2m1"
                                                     : "fp8_e4m3";
   const char* sname = p->scale_fmt == MOE_SCALE_F32 ? "f32" : (p->scale_fmt == MOE_SCALE_UE8M0 ? "ue8m0" : "none");
-  const char* kern = pl.path == kDecode ? "stream_weights_16tok_mfma16x16x32"
+  const char* kern = pl.path == kDecode ? "stream_16tok_mfma16x16x32_lds_dma_ring3"
                      : p->weight_dtype == MOE_F32 ? "fma_64x64"
                      : p->weight_dtype == MOE_BF16 ? "mfma32x32x16_bf16_160x256_k64_lds_dma_ring3"
                      : is_fp4(*p) ? "mfma16x16x128_e4m3xe2m1_scaled_128x256_ring3"
@@ -453,15 +455,15 @@ moe_status moe_experts_forward(const moe_problem* p, const void* hidden, const i
     MOE_HIP_CHECK(stage_mark(MOE_STAGE_QUANT_X, 1, s));
   }
 
-  const int64_t active_max = A < p->E ? A : p->E;
   if (pl.path == kDecode) {
-    gu.NT = p->I / 64;
-    dn.NT = p->H / 64;
+    gu.NT = p->I / decode_gateup_cols();
+    dn.NT = p->H / decode_down_cols();
+    const int64_t passes = max_mtiles(A, p->E, decode_bm());
     MOE_HIP_CHECK(stage_mark(MOE_STAGE_GATE_UP, 0, s));
-    MOE_HIP_CHECK(launch_decode_gateup(gu, persistent_grid(dev->cus, 2, active_max * gu.NT), s));
+    MOE_HIP_CHECK(launch_decode_gateup(gu, persistent_grid(dev->cus, decode_groups_per_cu(), passes * gu.NT), s));
     MOE_HIP_CHECK(stage_mark(MOE_STAGE_GATE_UP, 1, s));
     MOE_HIP_CHECK(stage_mark(MOE_STAGE_DOWN, 0, s));
-    MOE_HIP_CHECK(launch_decode_down(dn, persistent_grid(dev->cus, 2, active_max * dn.NT), s));
+    MOE_HIP_CHECK(launch_decode_down(dn, persistent_grid(dev->cus, decode_groups_per_cu(), passes * dn.NT), s));
     MOE_HIP_CHECK(stage_mark(MOE_STAGE_DOWN, 1, s));
   } else if (f32) {
     gu.NT = p->I / 32;

@@ -110,8 +110,14 @@ hipError_t launch_down_f32(const GroupedArgs& g, int64_t max_items, hipStream_t 
 
 // ---------------------------------------------------------------------------- decode path
 // Small-T path: each active expert's weights are streamed once from HBM against its
-// few rows held in LDS; work items are (expert, 64-column block), persistent grid.
+// few rows; one workgroup per work item (expert, pass of decode_bm() sorted rows, group
+// of decode_*_cols() output columns), persistent grid of decode_groups_per_cu()
+// workgroups per CU.  The routing tables are copied to LDS, so A = T * k <= kDecodeMaxSlots.
+constexpr int kDecodeMaxSlots = 2048;
 int decode_bm();
+int decode_gateup_cols();
+int decode_down_cols();
+int decode_groups_per_cu();
 hipError_t launch_decode_gateup(const GroupedArgs& g, int grid, hipStream_t s);
 hipError_t launch_decode_down(const GroupedArgs& g, int grid, hipStream_t s);
 
