@@ -399,9 +399,11 @@ moe_status moe_experts_forward(const moe_problem* p, const void* hidden, const i
   r.bm0 = pl.bm;
   r.mt0 = mt;
   r.part = reinterpret_cast<int32_t*>(ws + L.route_part);
-  MOE_HIP_CHECK(stage_mark(MOE_STAGE_ROUTE, 0, s));
-  MOE_HIP_CHECK(launch_route(r, s));
-  MOE_HIP_CHECK(stage_mark(MOE_STAGE_ROUTE, 1, s));
+  if (pl.path != kDecode) {   // (the decode kernels route in LDS themselves)
+    MOE_HIP_CHECK(stage_mark(MOE_STAGE_ROUTE, 0, s));
+    MOE_HIP_CHECK(launch_route(r, s));
+    MOE_HIP_CHECK(stage_mark(MOE_STAGE_ROUTE, 1, s));
+  }
 
   GroupedArgs g{};
   g.E = p->E;
@@ -458,6 +460,10 @@ moe_status moe_experts_forward(const moe_problem* p, const void* hidden, const i
   if (pl.path == kDecode) {
     gu.NT = p->I / decode_gateup_cols();
     dn.NT = p->H / decode_down_cols();
+    gu.topk_idx = dn.topk_idx = topk_idx;
+    gu.A_slots = dn.A_slots = (int)A;
+    gu.inv_out = inv;   // for the slot-order combine
+    gu.bad_out = bad;
     const int64_t passes = max_mtiles(A, p->E, decode_bm());
     MOE_HIP_CHECK(stage_mark(MOE_STAGE_GATE_UP, 0, s));
     MOE_HIP_CHECK(launch_decode_gateup(gu, persistent_grid(dev->cus, decode_groups_per_cu(), passes * gu.NT), s));

@@ -20,8 +20,9 @@
 // four waves; rows past the pass's last row repeat it, and their results are dropped)
 // and the four weight tiles.  In a slot, the 16-byte chunk c of tile row r sits at chunk
 // c ^ (r & 15) of its row, so the 16 lanes of a fragment read hit 16 different banks.
-// Every table an item needs (M-tile starts, offsets, the sorted permutation, routing
-// weights) is copied to LDS first, so finding the next item never waits for the loads in
+// Every table an item needs (pass starts, offsets, the sorted permutation, routing
+// weights) is built in LDS first (route_in_lds, below: the decode path launches no
+// separate routing kernel), so finding the next item never waits for the loads in
 // flight.
 //
 // v_mfma_f32_16x16x32_bf16 takes the weights as the 16-row A operand and the tokens as
@@ -50,6 +51,79 @@ struct Item {
   int e, row0, nt, cg;
 };
 
+// Routing bookkeeping of the decode path, in LDS, by every workgroup of both decode
+// kernels (the same deterministic steps on the same ids, so all of them obtain the
+// order the routing kernel would): expert counts, exclusive-scan offsets and pass
+// starts, and the stable rank of each slot among the slots of its expert.  Wave 0
+// ranks 64 slots per round in slot order: lanes holding the same expert are found with
+// one ballot per bit of (expert + 1) (out-of-range ids form a group of their own that
+// is dropped), a lane's rank is its count of such lanes below it plus the expert's
+// running count, and the group's last lane advances that count.
+__device__ __forceinline__ void route_in_lds(const int32_t* __restrict__ idx, int A, int E, int* sIdx, int* sRank, int* sCnt,
+                             int* sOff, int* sMt, int* sBad) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  for (int a = tid; a < A; a += kThreads) sIdx[a] = idx[a];
+  for (int e = tid; e < E; e += kThreads) sCnt[e] = 0;
+  __syncthreads();
+  if (tid < kWave) {
+    int bad = 0;
+    for (int a0 = 0; a0 < A; a0 += kWave) {
+      const int a = a0 + lane;
+      const int e = a < A ? sIdx[a] : -1;
+      const bool valid = a < A && e >= 0 && e < E;
+      bad += __popcll(__ballot(a < A && !valid));
+      const int key = valid ? e + 1 : 0;   // <= 1024: 11 bits
+      uint64_t same = ~0ull;
+#pragma unroll
+      for (int bit = 0; bit < 11; ++bit) {
+        const uint64_t on = __ballot((key >> bit) & 1);
+        same &= ((key >> bit) & 1) ? on : ~on;
+      }
+      const int below = __popcll(same & ((1ull << lane) - 1ull));
+      if (valid) {
+        const int base = sCnt[e];
+        sRank[a] = base + below;
+        if ((same >> lane) == 1ull) sCnt[e] = base + below + 1;   // last lane of the group
+      }
+    }
+    // exclusive scans of the counts (offsets) and of the 16-row passes (pass starts)
+    const int per = (E + kWave - 1) / kWave;
+    int sc = 0, sm = 0;
+    for (int i = 0; i < per; ++i) {
+      const int e = lane * per + i;
+      if (e < E) {
+        sc += sCnt[e];
+        sm += (sCnt[e] + kTok - 1) / kTok;
+      }
+    }
+    int ic = sc, im = sm;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int tc = __shfl_up(ic, d), tm = __shfl_up(im, d);
+      if (lane >= d) {
+        ic += tc;
+        im += tm;
+      }
+    }
+    int oc = ic - sc, om = im - sm;
+    for (int i = 0; i < per; ++i) {
+      const int e = lane * per + i;
+      if (e < E) {
+        sOff[e] = oc;
+        sMt[e] = om;
+        oc += sCnt[e];
+        om += (sCnt[e] + kTok - 1) / kTok;
+      }
+    }
+    if (lane == kWave - 1) {
+      sOff[E] = ic;
+      sMt[E] = im;
+      *sBad = bad;
+    }
+  }
+  __syncthreads();
+}
+
 template <int MODE, int KC>
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(GroupedArgs g) {
   constexpr int RB = KC * 2;              // bytes of one row in a slot
@@ -72,19 +146,30 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(GroupedArgs g) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int E = g.E;
-  const int A = g.offsets[E];
-  for (int i = tid; i <= E; i += kThreads) {
-    sMt[i] = g.mt[i];
-    sOff[i] = g.offsets[i];
-  }
-  for (int p = tid; p < A; p += kThreads) {
-    if (MODE == kGateUp) {
-      sRow[p] = g.perm[p] / g.k;
-    } else {
-      const int slot = g.perm[p];
-      sRow[p] = slot;
-      sWt[p] = g.topk_w[slot];
+  {
+    // the ring is free until the first DMA: it holds the routing scratch meanwhile
+    int* sIdx = reinterpret_cast<int*>(ring);
+    int* sRank = sIdx + kDecodeMaxSlots;
+    int* sCnt = sRank + kDecodeMaxSlots;
+    int* sBad = sCnt + kMaxE;
+    const int A = g.A_slots;
+    route_in_lds(g.topk_idx, A, E, sIdx, sRank, sCnt, sOff, sMt, sBad);
+    const bool publish = MODE == kGateUp && blockIdx.x == 0;   // inv and the bad-id count
+    for (int a = tid; a < A; a += kThreads) {
+      const int e = sIdx[a];
+      const bool valid = e >= 0 && e < E;
+      const int p = valid ? sOff[e] + sRank[a] : -1;
+      if (valid) {
+        if (MODE == kGateUp) {
+          sRow[p] = a / g.k;
+        } else {
+          sRow[p] = a;
+          sWt[p] = g.topk_w[a];
+        }
+      }
+      if (publish) g.inv_out[a] = p;
     }
+    if (publish && tid == 0 && g.bad_out != nullptr) *g.bad_out = *sBad;
   }
   __syncthreads();
 

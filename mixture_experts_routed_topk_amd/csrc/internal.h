@@ -76,6 +76,13 @@ struct GroupedArgs {
   float* zero_out;
   int64_t zero_n4;
   int gate;                 // gate function of the gated activation (kGate*)
+  // decode path only: the kernels route in LDS themselves from the [A] expert ids;
+  // the gate/up kernel also writes inv [A] (sorted position or -1) and the number of
+  // out-of-range ids (bad_out, may be null)
+  const int32_t* topk_idx;
+  int A_slots;
+  int32_t* inv_out;
+  int32_t* bad_out;
 };
 
 // Upper bound on M tiles for a tile height (host-side grid sizing).

@@ -133,6 +133,15 @@ def test_forward_rejects_before_any_hip_call():
     st = L.moe_experts_forward(ctypes.byref(p4), fake, fake, fake, fake, fake, fake, fake, fake,
                                fake, 1 << 40, None)
     assert st == m.ERR_UNSUPPORTED
+    # the decode path holds its routing tables in LDS: at most 2048 slots
+    pd = P(act=m.BF16, weight=m.BF16, T=64, k=33, E=64, I=128, flags=m.FLAG_FORCE_DECODE)
+    st = L.moe_experts_forward(ctypes.byref(pd), fake, fake, fake, fake, fake, None, None, fake,
+                               fake, 1 << 40, None)
+    assert st == m.ERR_UNSUPPORTED
+    pd.k = 32
+    s = ctypes.create_string_buffer(512)
+    assert L.moe_plan_describe(ctypes.byref(pd), s, 512) == m.OK
+    assert b"path=decode" in s.value
     # null problem
     assert L.moe_experts_forward(None, fake, fake, fake, fake, fake, None, None, fake, fake,
                                  1 << 40, None) == m.ERR_NULL_ARG

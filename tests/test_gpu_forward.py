@@ -157,6 +157,34 @@ def test_decode_shapes(shape):
     _full_check(spec, m.FLAG_FORCE_DECODE)
 
 
+def test_decode_most_slots():
+    # T * k = 2048, the decode path's limit: 32 rounds of the in-LDS ranking, and 51 slots
+    # per expert on average, so several 16-row passes per expert
+    spec = synth.Spec("decode_max", T=64, H=256, I=128, E=40, k=32, act="bf16", weight="bf16", renorm=True,
+                      seed=13)
+    _full_check(spec, m.FLAG_FORCE_DECODE)
+
+
+def test_decode_bad_index_and_repeatability():
+    spec = synth.Spec("bad_dec", T=40, H=128, I=128, E=4, k=2, act="bf16", weight="bf16", seed=4)
+    D = device_layer(spec, poison_inactive=False)
+    D["idx"][7, 1] = 4
+    D["idx"][11, 0] = -1
+    with pytest.raises(IndexError):
+        _run(D, m.FLAG_CHECK_INDICES | m.FLAG_FORCE_DECODE)
+    # without the flag the slots contribute nothing
+    out = gpu_out_f64(_run(D, m.FLAG_FORCE_DECODE))
+    w = D["w_host"].copy()
+    idx = D["idx_host"].copy()
+    w[7, 1] = w[11, 0] = 0.0
+    idx[7, 1] = idx[11, 0] = 0
+    ref = oracle_out(spec, D["x_host"], idx, w, oracle_weights(spec))
+    assert_close(out, ref, "bf16", "out-of-range slots ignored on the decode path")
+    a = _run(D, m.FLAG_DETERMINISTIC | m.FLAG_FORCE_DECODE).clone()
+    b = _run(D, m.FLAG_DETERMINISTIC | m.FLAG_FORCE_DECODE)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
 def test_decode_matches_grouped_on_tiny_prefill():
     # both paths on the same 96-token layer
     spec = synth.Spec("both", T=96, H=256, I=128, E=6, k=2, act="bf16", weight="bf16", seed=12)
