@@ -15,7 +15,10 @@ namespace moe {
 namespace {
 
 constexpr int kMaxDevices = 64;
-constexpr int64_t kDecodeMaxTokens = 64;
+// The decode path is chosen by default while the experts average at most one 16-row pass
+// (T * k <= 16 * E): measured on the Qwen-shaped layer (E = 60, k = 4) it is faster than the
+// grouped path up to T = 192 and slower from T = 256 on.
+constexpr int64_t kDecodeMaxSlotsPerExpert = 16;
 
 struct DeviceRecord {
   bool ready = false;
@@ -107,7 +110,7 @@ bool decode_capable(const moe_problem& p) {
 
 Plan make_plan(const moe_problem& p) {
   Plan pl;
-  bool decode = p.T <= kDecodeMaxTokens;
+  bool decode = p.T * p.k <= kDecodeMaxSlotsPerExpert * p.E;
   if (p.flags & MOE_FLAG_FORCE_GROUPED) decode = false;
   if (p.flags & MOE_FLAG_FORCE_DECODE) decode = true;
   if (!decode_capable(p)) decode = false;

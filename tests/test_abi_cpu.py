@@ -168,6 +168,11 @@ def test_plan_describe():
     s = m.plan_describe(P(act=m.BF16, weight=m.BF16, T=16, H=2048, I=1408, E=60, k=4,
                           flags=m.FLAG_FORCE_GROUPED))
     assert "path=grouped" in s
+    # the default switch: decode while T * k <= 16 * E
+    s = m.plan_describe(P(act=m.BF16, weight=m.BF16, T=240, H=2048, I=1408, E=60, k=4))
+    assert "path=decode" in s
+    s = m.plan_describe(P(act=m.BF16, weight=m.BF16, T=241, H=2048, I=1408, E=60, k=4))
+    assert "path=grouped" in s
     s = m.plan_describe(P(act=m.BF16, weight=m.FP4_E2M1, scale=m.SCALE_UE8M0, T=16, H=7168, I=2048,
                           E=256, k=8))
     assert "path=grouped" in s and "weights=fp4_e2m1" in s and "scales=ue8m0" in s
