@@ -76,8 +76,8 @@ enum {
   /* Path selection (both give the same result within tolerance): the grouped
    * path sorts slots by expert and runs grouped GEMMs; the decode path streams
    * each selected expert's weights once against its few tokens.  Default: decode
-   * when T * k <= 16 * E (at most one 16-row pass per expert on average) and the
-   * decode path takes the problem, grouped otherwise.  The decode path takes bf16 weights with
+   * when T * k <= min(16 * E, 512) (at most one 16-row pass per expert on average)
+   * and the decode path takes the problem, grouped otherwise.  The decode path takes bf16 weights with
    * I % 128 == 0 and T * k <= 2048 (its routing tables live in LDS); forcing it
    * on any other problem returns MOE_ERR_UNSUPPORTED. */
   MOE_FLAG_FORCE_GROUPED = 4u,

@@ -16,9 +16,13 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 // The decode path is chosen by default while the experts average at most one 16-row pass
-// (T * k <= 16 * E): measured on the Qwen-shaped layer (E = 60, k = 4) it is faster than the
-// grouped path up to T = 192 and slower from T = 256 on.
+// and the batch has at most 512 slots (T * k <= min(16 E, 512)).  Measured: on the Qwen-shaped
+// layer (E = 60, k = 4, uniform routing) the decode path is faster than the grouped path up to
+// T = 192 and slower from T = 256; on the DeepSeek-shaped layer (E = 256, k = 8, Zipf-skewed)
+// it is faster at T = 16 and 4% slower at T = 64, 17% at T = 128 (hot experts need many 16-row
+// passes, each streaming the expert's weights again).
 constexpr int64_t kDecodeMaxSlotsPerExpert = 16;
+constexpr int64_t kDecodeDefaultMaxSlots = 512;
 
 struct DeviceRecord {
   bool ready = false;
@@ -110,7 +114,7 @@ bool decode_capable(const moe_problem& p) {
 
 Plan make_plan(const moe_problem& p) {
   Plan pl;
-  bool decode = p.T * p.k <= kDecodeMaxSlotsPerExpert * p.E;
+  bool decode = p.T * p.k <= kDecodeMaxSlotsPerExpert * p.E && p.T * p.k <= kDecodeDefaultMaxSlots;
   if (p.flags & MOE_FLAG_FORCE_GROUPED) decode = false;
   if (p.flags & MOE_FLAG_FORCE_DECODE) decode = true;
   if (!decode_capable(p)) decode = false;

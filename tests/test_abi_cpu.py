@@ -168,10 +168,12 @@ def test_plan_describe():
     s = m.plan_describe(P(act=m.BF16, weight=m.BF16, T=16, H=2048, I=1408, E=60, k=4,
                           flags=m.FLAG_FORCE_GROUPED))
     assert "path=grouped" in s
-    # the default switch: decode while T * k <= 16 * E
-    s = m.plan_describe(P(act=m.BF16, weight=m.BF16, T=240, H=2048, I=1408, E=60, k=4))
+    # the default switch: decode while T * k <= min(16 * E, 512)
+    s = m.plan_describe(P(act=m.BF16, weight=m.BF16, T=128, H=2048, I=1408, E=60, k=4))
     assert "path=decode" in s
-    s = m.plan_describe(P(act=m.BF16, weight=m.BF16, T=241, H=2048, I=1408, E=60, k=4))
+    s = m.plan_describe(P(act=m.BF16, weight=m.BF16, T=129, H=2048, I=1408, E=60, k=4))
+    assert "path=grouped" in s
+    s = m.plan_describe(P(act=m.BF16, weight=m.BF16, T=33, H=256, I=128, E=2, k=1))   # > 16 E
     assert "path=grouped" in s
     s = m.plan_describe(P(act=m.BF16, weight=m.FP4_E2M1, scale=m.SCALE_UE8M0, T=16, H=7168, I=2048,
                           E=256, k=8))
