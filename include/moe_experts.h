@@ -161,6 +161,12 @@ moe_status moe_workspace_size(const moe_problem* p, size_t* bytes);
  * Returns MOE_OK once the work is enqueued (T == 0: nothing is enqueued).
  * Errors: NULL_ARG, BAD_SHAPE, UNSUPPORTED, WORKSPACE_TOO_SMALL before any HIP
  * call; BAD_INDEX only with MOE_FLAG_CHECK_INDICES (after a stream sync); HIP.
+ *
+ * Stream capture: without MOE_FLAG_CHECK_INDICES the call only launches kernels on
+ * `stream` (no host wait, no memset, no allocation), with grids fixed by T, k, E, H
+ * and I, so it can be captured into a HIP graph once (after one call outside the
+ * capture on the device) and replayed for any ids and weights written into the same
+ * buffers.
  */
 moe_status moe_experts_forward(const moe_problem* p, const void* hidden, const int32_t* topk_idx,
                                const float* topk_w, const void* w_gate_up, const void* w_down,
