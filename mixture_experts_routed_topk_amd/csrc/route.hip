@@ -309,13 +309,19 @@ __global__ __launch_bounds__(kRouteThreads) void route_place_kernel(RouteArgs p)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) hist[i] = 0;
-  // expert totals and the counts of earlier chunks, from the count pass
+  // expert totals and the counts of earlier chunks, from the count pass (the G loads of
+  // an expert are issued eight at a time, not one after the other)
   for (int e = tid; e < E; e += kRouteThreads) {
     int tot = 0, before = 0;
-    for (int q = 0; q < G; ++q) {
-      const int c = p.part[(int64_t)q * E + e];
-      tot += c;
-      before += q < g ? c : 0;
+    for (int q0 = 0; q0 < G; q0 += 8) {
+      int c[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) c[u] = q0 + u < G ? p.part[(int64_t)(q0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        tot += c[u];
+        before += q0 + u < g ? c[u] : 0;
+      }
     }
     offs[e] = tot;
     tiles[e] = before;
@@ -339,7 +345,13 @@ __global__ __launch_bounds__(kRouteThreads) void route_place_kernel(RouteArgs p)
     p.offsets[E] = valid;
     if (p.bad) {
       int nb = 0;
-      for (int q = 0; q < G; ++q) nb += p.part[(int64_t)G * E + q];
+      for (int q0 = 0; q0 < G; q0 += 8) {
+        int c[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) c[u] = q0 + u < G ? p.part[(int64_t)G * E + q0 + u] : 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) nb += c[u];
+      }
       *p.bad = nb;
     }
   }
