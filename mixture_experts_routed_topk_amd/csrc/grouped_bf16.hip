@@ -79,7 +79,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_bf16_kernel(GroupedArgs g
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
   const int hgrp = lane >> 5, r32 = lane & 31;
-  const int gx = gridDim.x >> 3;
   const int xcd = blockIdx.x & 7, xslot = blockIdx.x >> 3;
   const int E = g.E;
   const int KT = g.K / KS;
@@ -94,6 +93,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_bf16_kernel(GroupedArgs g
     for (int i = tid; i <= E; i += kThreads) sMt[i] = (uint16_t)g.mt[i];
   __syncthreads();
   const int n_items = n_mt * g.NT;
+  // as few workgroups take items as still finish them in the least number of rounds, the
+  // same number on every XCD (fewer tiles in flight at once shorten each tile's operand
+  // stream); workgroup b takes items (b & 7) gx + (b >> 3) + 8 gx j when (b >> 3) < gx
+  const int rounds = max(1, (n_items + (int)gridDim.x - 1) / (int)gridDim.x);
+  const int gx = ((n_items + rounds - 1) / rounds + 7) >> 3;
   auto mt_at = [&](int i) __attribute__((always_inline)) -> int { return mt_lds ? (int)sMt[i] : g.mt[i]; };
 
   // DMA lane L of the instruction for row block b (RPI rows) fills chunk slot (L & 7) of
@@ -115,7 +119,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_bf16_kernel(GroupedArgs g
 
   f32x16 acc[MFRAG][NFRAG];
 
-  for (int w = xcd * gx + xslot; w < n_items; w += gridDim.x) {
+  for (int w = xslot < gx ? xcd * gx + xslot : n_items; w < n_items; w += 8 * gx) {
     // ---- the tile of work item w
     int e;
     {
