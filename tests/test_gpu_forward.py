@@ -159,6 +159,19 @@ def test_decode_shapes(shape):
     _full_check(spec, m.FLAG_FORCE_DECODE)
 
 
+@pytest.mark.parametrize("T,flags", [(16, 0), (64, m.FLAG_FORCE_DECODE)])
+def test_dsv3_shaped_decode(T, flags):
+    # the DeepSeek-V3-shaped bf16 layer with few tokens: K steps of 256 in both decode GEMMs,
+    # Zipf-skewed routing (T = 64: hot experts take several 16-row passes)
+    spec = synth.spec_for("dsv3_prefill_bf16", T=T)
+    D = device_layer(spec)
+    prob = m.problem_for(D["x"], D["idx"], D["w_gate_up"], D["w_down"], flags=flags)
+    assert "path=decode" in m.plan_describe(prob)
+    out = gpu_out_f64(_run(D, flags))
+    ref = oracle_out(spec, D["x_host"], D["idx_host"], D["w_host"], prefetched_weights(spec, D["active"]))
+    assert_close(out, ref, "bf16", f"dsv3-shaped decode T={T}")
+
+
 def test_decode_most_slots():
     # T * k = 2048, the decode path's limit: 32 rounds of the in-LDS ranking, and 51 slots
     # per expert on average, so several 16-row passes per expert
