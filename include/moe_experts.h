@@ -69,9 +69,10 @@ enum {
   MOE_FLAG_CHECK_INDICES = 1u,
   /* Bit-reproducible combine at every size: each slot's weighted expert output is
    * written to its own row and the k rows of a token are summed in slot order.
-   * Without the flag this combine is used while the slot rows (4*T*k*H bytes) are at
-   * most 512 MiB, and floating-point atomic adds into a [T, H] accumulator above (or
-   * always with MOE_FLAG_ATOMIC_COMBINE). */
+   * Without the flag this combine is used while the slot rows are small (float32
+   * rows, 4*T*k*H bytes, at most 512 MiB; the bf16 rows of a bf16 layer, 2*T*k*H
+   * bytes, at most 1 GiB), and floating-point atomic adds into a [T, H] accumulator
+   * above (or always with MOE_FLAG_ATOMIC_COMBINE). */
   MOE_FLAG_DETERMINISTIC = 2u,
   /* Path selection (both give the same result within tolerance): the grouped
    * path sorts slots by expert and runs grouped GEMMs; the decode path streams
@@ -123,8 +124,9 @@ const char* moe_status_str(moe_status s);
 /* Bytes of device workspace moe_experts_forward needs for problem *p (host only,
  * closed form, no HIP call).  Grows with T*k*(I + H) and T*H.  When the k rows of a
  * token are combined as per-slot rows (always with MOE_FLAG_DETERMINISTIC; by default
- * while 4*T*k*H <= 512 MiB, where that combine is the faster one; never with
- * MOE_FLAG_ATOMIC_COMBINE) it holds a [T*k, H] buffer instead of the float32 [T, H]
+ * while 4*T*k*H <= 512 MiB, or 2*T*k*H <= 1 GiB for a bf16 layer, where that combine is
+ * the faster one; never with MOE_FLAG_ATOMIC_COMBINE) it holds a [T*k, H] buffer instead
+ * of the float32 [T, H]
  * accumulator: float32 rows with MOE_FLAG_DETERMINISTIC, and bf16 rows (each slot's
  * weighted row rounded once, the k rows summed in float32) on the default bf16
  * grouped path. */

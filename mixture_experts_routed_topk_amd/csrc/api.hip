@@ -87,14 +87,21 @@ struct Plan {
 
 // Combine by per-slot rows (each slot's weighted row stored, the k rows of a token summed
 // in slot order) rather than float atomics: always with MOE_FLAG_DETERMINISTIC, and by
-// default while the slot rows stay small.  Measured on MI355X: with 134 MB of slot rows
-// (Qwen prefill, T*k = 16384, H = 2048) the down kernel plus the slot sum take 12% less
-// time than the atomic combine; with 1.9 GB (DeepSeek prefill) the atomics win by 3%.
+// default while the slot rows stay small: float32 rows up to 512 MiB, the bf16 rows of a
+// bf16 layer up to 1 GiB.  Measured on MI355X: with 134 MB of slot rows (Qwen prefill,
+// T*k = 16384, H = 2048) the down kernel plus the slot sum take 12% less time than the
+// atomic combine; on the DeepSeek prefill layer (T*k = 65536, H = 7168) float32 rows
+// (1.9 GB) lose to the atomics by 3%, bf16 rows (0.94 GB) win by 1.4% of the whole step.
 constexpr int64_t kSlotCombineMaxBytes = int64_t(512) << 20;
+constexpr int64_t kSlotCombineMaxBytesBf16 = int64_t(1) << 30;
 bool slot_combine(const moe_problem& p) {
   if (p.flags & MOE_FLAG_DETERMINISTIC) return true;
   if (p.flags & MOE_FLAG_ATOMIC_COMBINE) return false;
-  return 4 * (int64_t)p.T * p.k * p.H <= kSlotCombineMaxBytes;
+  const int64_t rows = (int64_t)p.T * p.k * p.H;
+  if (4 * rows <= kSlotCombineMaxBytes) return true;
+  // larger bf16 layers take the grouped path (the decode path stops at T * k <= 2048),
+  // whose default slot rows are bf16
+  return p.weight_dtype == MOE_BF16 && p.act_dtype == MOE_BF16 && 2 * rows <= kSlotCombineMaxBytesBf16;
 }
 
 // The per-slot rows of the bf16 grouped path's default combine are stored as bf16: each

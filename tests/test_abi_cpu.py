@@ -93,12 +93,20 @@ def test_workspace_by_combine():
     A, H, T = 4096 * 4, 2048, 4096
     assert n_det - n_default == 2 * A * H        # default: bf16 slot rows; deterministic: float32
     assert n_det - n_atomic == 4 * A * H - 4 * T * H
-    # above 512 MiB of slot rows the default is the atomic combine
+    # bf16 layers keep bf16 slot rows up to 1 GiB of them (the DeepSeek-shaped layer: 0.94 GB) ...
     big = P(act=m.BF16, weight=m.BF16, T=8192, H=7168, I=2048, E=256, k=8)
     _, nb_default = _ws(big)
     big.flags = m.FLAG_ATOMIC_COMBINE
     _, nb_atomic = _ws(big)
-    assert nb_default == nb_atomic
+    Ab, Hb, Tb = 8192 * 8, 7168, 8192
+    assert nb_default - nb_atomic == 2 * Ab * Hb - 4 * Tb * Hb
+    assert "combine=slot_rows_bf16" in m.plan_describe(P(act=m.BF16, weight=m.BF16, T=8192, H=7168, I=2048,
+                                                         E=256, k=8))
+    # ... and above that, or for float32 rows above 512 MiB, the default is the atomic combine
+    bigger = P(act=m.BF16, weight=m.BF16, T=9363, H=7168, I=2048, E=256, k=8)   # 2*T*k*H > 1 GiB
+    assert "combine=atomic_f32" in m.plan_describe(bigger)
+    fp8 = P(act=m.BF16, weight=m.FP8_E4M3, scale=m.SCALE_F32, T=4096, H=7168, I=2048, E=256, k=8)
+    assert "combine=atomic_f32" in m.plan_describe(fp8)
     p.flags = m.FLAG_DETERMINISTIC | m.FLAG_ATOMIC_COMBINE
     assert _ws(p)[0] == m.ERR_UNSUPPORTED
 
