@@ -16,7 +16,7 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "experts_forward", "route", "route_logits", "quantize_rows_fp8", "workspace_size", "plan_describe",
+    "experts_forward", "check_scales", "check_mfma_blocks", "route", "route_logits", "quantize_rows_fp8", "workspace_size", "plan_describe",
     "Problem", "MoeError", "lib", "FLAG_CHECK_INDICES", "FLAG_DETERMINISTIC", "FLAG_ATOMIC_COMBINE", "FLAG_ACT_GELU", "FLAG_ACT_RELU",
     "FLAG_FORCE_GROUPED", "FLAG_FORCE_DECODE", "LIB_PATH",
 ]
@@ -40,7 +40,7 @@ FLAG_ACT_RELU = 64
 
 EXPORTS = ["moe_abi_version", "moe_status_str", "moe_workspace_size", "moe_experts_forward",
            "moe_route", "moe_route_logits", "moe_quantize_rows_fp8", "moe_plan_describe",
-           "moe_set_stage_events"]
+           "moe_set_stage_events", "moe_check_mfma_blocks"]
 
 # stage ids (moe_set_stage_events)
 STAGES = ["zero", "route", "quant_x", "gate_up", "quant_act", "down", "finalize"]
@@ -89,6 +89,8 @@ def lib():
     L.moe_quantize_rows_fp8.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, vp, vp, vp]
     L.moe_plan_describe.restype = ctypes.c_int
     L.moe_plan_describe.argtypes = [P, ctypes.c_char_p, sz]
+    L.moe_check_mfma_blocks.restype = ctypes.c_int
+    L.moe_check_mfma_blocks.argtypes = [ctypes.c_int, vp, vp, vp, vp, ctypes.c_int, vp]
     L.moe_set_stage_events.restype = ctypes.c_int
     L.moe_set_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
     _lib = L
@@ -166,6 +168,37 @@ def problem_for(hidden, topk_idx, w_gate_up, w_down, w_gate_up_scale=None, flags
     return Problem(T, H, twoI // 2, E, k, _ACT[hidden.dtype], weight, scale, flags)
 
 
+def check_scales(prob: Problem, w_gate_up_scale: Optional[torch.Tensor],
+                 w_down_scale: Optional[torch.Tensor]) -> None:
+    """Block scales must match the weight format exactly, since the kernels read them by index.
+
+    e4m3 weights: [E, 2I/128, H/128] and [E, H/128, I/128], both float32 or both uint8 (UE8M0);
+    fp4 weights: [E, 2I, H/32] and [E, H, I/32] uint8 (UE8M0); other weights take none.
+    Raises ValueError on a missing, extra, mismatched or wrongly shaped scale tensor.
+    """
+    E, H, I = prob.E, prob.H, prob.I
+    if prob.weight_dtype not in (FP8_E4M3, FP4_E2M1):
+        if w_gate_up_scale is not None or w_down_scale is not None:
+            raise ValueError("block scales are only taken with e4m3 or fp4 weights")
+        return
+    if w_gate_up_scale is None or w_down_scale is None:
+        raise ValueError("e4m3 and fp4 weights need both w_gate_up_scale and w_down_scale")
+    if w_gate_up_scale.dtype != w_down_scale.dtype:
+        raise ValueError(f"scale dtypes differ: {w_gate_up_scale.dtype} and {w_down_scale.dtype}")
+    if prob.weight_dtype == FP4_E2M1:
+        if w_gate_up_scale.dtype != torch.uint8:
+            raise ValueError("fp4 weights take UE8M0 (uint8) scales")
+        want = ((E, 2 * I, H // 32), (E, H, I // 32))
+    else:
+        if w_gate_up_scale.dtype not in (torch.float32, torch.uint8):
+            raise ValueError("e4m3 block scales must be float32 or uint8 (UE8M0)")
+        want = ((E, 2 * I // 128, H // 128), (E, H // 128, I // 128))
+    for name, t, shape in (("w_gate_up_scale", w_gate_up_scale, want[0]),
+                           ("w_down_scale", w_down_scale, want[1])):
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
+
+
 def experts_forward(hidden: torch.Tensor, topk_idx: torch.Tensor, topk_w: torch.Tensor,
                     w_gate_up: torch.Tensor, w_down: torch.Tensor,
                     w_gate_up_scale: Optional[torch.Tensor] = None,
@@ -189,6 +222,7 @@ def experts_forward(hidden: torch.Tensor, topk_idx: torch.Tensor, topk_w: torch.
     if topk_w.shape != topk_idx.shape:
         raise ValueError("topk_w and topk_idx shapes differ")
     prob = problem_for(hidden, topk_idx, w_gate_up, w_down, w_gate_up_scale, flags)
+    check_scales(prob, w_gate_up_scale, w_down_scale)
     for name, t in (("w_gate_up_scale", w_gate_up_scale), ("w_down_scale", w_down_scale)):
         if t is not None:
             _need_gpu(name, t)
@@ -275,3 +309,21 @@ def quantize_rows_fp8(x: torch.Tensor):
     s = torch.empty((R, C // 128), dtype=torch.float32, device=x.device)
     _check(lib().moe_quantize_rows_fp8(_ptr(x), R, C, _ptr(q), _ptr(s), _stream(x.device)))
     return q, s
+
+
+def check_mfma_blocks(a: torch.Tensor, b: torch.Tensor, b_scale: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Block products on the kernels' block-scaled MFMA (moe_check_mfma_blocks): a uint8
+    [n,16,128] e4m3 codes; b uint8 [n,16,128] e4m3 codes, or [n,16,64] packed e2m1 with
+    b_scale uint8 [n,16,4] UE8M0.  Returns float32 [n,16,16]."""
+    fmt = 0 if b_scale is None else 1
+    for name, t in (("a", a), ("b", b)) + ((("b_scale", b_scale),) if fmt else ()):
+        _need_gpu(name, t)
+        if t.dtype != torch.uint8:
+            raise ValueError(f"{name} must be uint8")
+    n = a.shape[0]
+    want_b = (n, 16, 128) if fmt == 0 else (n, 16, 64)
+    if tuple(a.shape) != (n, 16, 128) or tuple(b.shape) != want_b or (fmt and tuple(b_scale.shape) != (n, 16, 4)):
+        raise ValueError("shapes: a [n,16,128], b [n,16,128] (e4m3) or [n,16,64] with b_scale [n,16,4] (e2m1)")
+    d = torch.empty((n, 16, 16), dtype=torch.float32, device=a.device)
+    _check(lib().moe_check_mfma_blocks(fmt, _ptr(a), _ptr(b), _ptr(b_scale), _ptr(d), n, _stream(a.device)))
+    return d

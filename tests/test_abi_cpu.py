@@ -223,3 +223,45 @@ def test_route_logits_rejects_before_any_hip_call():
     assert st == m.ERR_NULL_ARG         # no logits
     st = L.moe_route_logits(ctypes.byref(p), fake, 0, fake, fake, fake, fake, fake, fake, fake, 16, None)
     assert st == m.ERR_WORKSPACE
+
+
+# ----------------------------------------------------------------------------- scale tensors
+
+def _scales(shape_gu, shape_dn, dtype_gu, dtype_dn=None):
+    import torch
+    return torch.zeros(shape_gu, dtype=dtype_gu), torch.zeros(shape_dn, dtype=dtype_dn or dtype_gu)
+
+
+def test_check_scales_accepts_the_exact_shapes():
+    import torch
+    E, H, I = 4, 256, 384
+    p8 = P(act=m.BF16, weight=m.FP8_E4M3, scale=m.SCALE_F32, E=E, H=H, I=I)
+    for dt in (torch.float32, torch.uint8):
+        m.check_scales(p8, *_scales((E, 2 * I // 128, H // 128), (E, H // 128, I // 128), dt))
+    p4 = P(act=m.BF16, weight=m.FP4_E2M1, scale=m.SCALE_UE8M0, E=E, H=H, I=I)
+    m.check_scales(p4, *_scales((E, 2 * I, H // 32), (E, H, I // 32), torch.uint8))
+    m.check_scales(P(act=m.BF16, weight=m.BF16), None, None)
+
+
+@pytest.mark.parametrize("case", ["mixed_dtypes", "short_gate_up", "short_down", "missing_down",
+                                  "fp4_float_scales", "fp4_short", "scales_on_bf16", "float64"])
+def test_check_scales_rejects(case):
+    import torch
+    E, H, I = 4, 256, 384
+    p8 = P(act=m.BF16, weight=m.FP8_E4M3, scale=m.SCALE_F32, E=E, H=H, I=I)
+    p4 = P(act=m.BF16, weight=m.FP4_E2M1, scale=m.SCALE_UE8M0, E=E, H=H, I=I)
+    gu8, dn8 = (E, 2 * I // 128, H // 128), (E, H // 128, I // 128)
+    gu4, dn4 = (E, 2 * I, H // 32), (E, H, I // 32)
+    args = {
+        # a float32 w_down_scale beside UE8M0 gate_up scales would be read as bytes
+        "mixed_dtypes": (p8, *_scales(gu8, dn8, torch.uint8, torch.float32)),
+        "short_gate_up": (p8, *_scales((E, 2 * I // 128 - 1, H // 128), dn8, torch.float32)),
+        "short_down": (p8, *_scales(gu8, (E - 1, H // 128, I // 128), torch.float32)),
+        "missing_down": (p8, _scales(gu8, dn8, torch.float32)[0], None),
+        "fp4_float_scales": (p4, *_scales(gu4, dn4, torch.float32)),
+        "fp4_short": (p4, *_scales(gu4, (E, H, I // 64), torch.uint8)),
+        "scales_on_bf16": (P(act=m.BF16, weight=m.BF16), *_scales(gu8, dn8, torch.float32)),
+        "float64": (p8, *_scales(gu8, dn8, torch.float64)),
+    }[case]
+    with pytest.raises(ValueError):
+        m.check_scales(*args)
