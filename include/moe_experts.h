@@ -122,7 +122,12 @@ int moe_abi_version(void);
 const char* moe_status_str(moe_status s);
 
 /* Bytes of device workspace moe_experts_forward needs for problem *p (host only,
- * closed form, no HIP call).  Grows with T*k*(I + H) and T*H.  When the k rows of a
+ * closed form, no HIP call).  The page's backend table sets the memory of the
+ * "grouped_mm" row (tokens sorted by expert, activations of the selected experts
+ * only) against the "batched_mm" row (the selected experts' parameters duplicated
+ * per token); this sizes the grouped form's buffers, which hold the sorted slots
+ * and their activations, never a copy of a weight.  Grows with T*k*(I + H) and T*H.
+ * Errors: NULL_ARG (p or bytes NULL), BAD_SHAPE / UNSUPPORTED as for the forward.  When the k rows of a
  * token are combined as per-slot rows (always with MOE_FLAG_DETERMINISTIC; by default
  * while 4*T*k*H <= 512 MiB, or 2*T*k*H <= 1 GiB for a bf16 layer, where that combine is
  * the faster one; never with MOE_FLAG_ATOMIC_COMBINE) it holds a [T*k, H] buffer instead
@@ -231,9 +236,40 @@ moe_status moe_route_logits(const moe_problem* p, const float* logits, int renor
 moe_status moe_quantize_rows_fp8(const void* x_bf16, int64_t rows, int32_t cols, uint8_t* q,
                                  float* scales, void* stream);
 
-/* Describe the plan (path, tile shapes, workspace) chosen for *p into buf (NUL
- * terminated, truncated to len).  Host only. */
+/* Describe the plan chosen for *p into buf (NUL terminated, truncated to len):
+ * the path ("grouped" or "decode"), weight and scale formats, activation, combine,
+ * tile shapes and workspace bytes.  Host only, no HIP call.  This is the library's
+ * counterpart of the page's get_experts_implementation() ("Set an experts backend"
+ * section), which reports the experts backend a model will run with; here the
+ * choice between the sort-then-group path and the few-token decode path ("Decode
+ * stage switch" section) is made per call from T, k, E and the flags, and this
+ * reports it.  For fp8 and fp4 weights it also gives act_codes_offset and
+ * act_scales_offset: byte offsets into the forward's workspace of the e4m3 SwiGLU
+ * rows [T*k][I] (uint8) and their scales [T*k][I/128] (float32), in expert-sorted
+ * slot order (the order of moe_route's perm); they hold the last forward's values
+ * until the workspace is reused.  Errors: NULL_ARG (p or buf NULL, or len == 0),
+ * BAD_SHAPE / UNSUPPORTED as for the forward. */
 moe_status moe_plan_describe(const moe_problem* p, char* buf, size_t len);
+
+/*
+ * Instruction check (test export): nblocks independent block products on the block-scaled
+ * 16x16x128 MFMA that the e4m3 and FP4 grouped kernels use for each 128-long block of
+ * their dot products ("FP8 and FP4 quantized experts" section: the fp8 and fp4 expert
+ * GEMMs), with the same operand layout and a zero accumulator.  It exists so that the
+ * instruction's accumulation can be compared with exact sums; the parity window of the
+ * requantised SwiGLU rows rests on that comparison.
+ *
+ *   fmt 0: a [nblocks][16][128] e4m3 codes, b [nblocks][16][128] e4m3 codes;
+ *   fmt 1: a as above, b [nblocks][16][64] bytes of e2m1 codes (element k in the low
+ *          nibble of byte k/2 for even k), b_scale [nblocks][16][4] UE8M0 exponents (one
+ *          per column and 32-long k block);
+ *   d [nblocks][16][16] float32 out: d[i][r][n] = sum_k a[i][r][k] * b[i][n][k] (fmt 1:
+ *          times 2^(b_scale[i][n][k/32] - 127)).
+ * Device pointers; a and b 16-byte aligned.  Errors: UNSUPPORTED (fmt), BAD_SHAPE,
+ * NULL_ARG, HIP.  Asynchronous on `stream`.
+ */
+moe_status moe_check_mfma_blocks(int fmt, const uint8_t* a, const uint8_t* b, const uint8_t* b_scale, float* d,
+                                 int nblocks, void* stream);
 
 /* Stages of one forward, in launch order (a stage a path does not use is skipped). */
 enum {
@@ -241,7 +277,8 @@ enum {
   MOE_STAGE_ROUTE = 1,     /* routing bookkeeping                                */
   MOE_STAGE_QUANT_X = 2,   /* fp8 only: quantise the hidden states               */
   MOE_STAGE_GATE_UP = 3,   /* gate/up projection + SwiGLU                        */
-  MOE_STAGE_QUANT_ACT = 4, /* fp8 only: quantise the SwiGLU output               */
+  MOE_STAGE_QUANT_ACT = 4, /* not launched: fp8 / fp4 gate_up kernels quantise the
+                              SwiGLU output in their epilogue                    */
   MOE_STAGE_DOWN = 5,      /* down projection + routing weight + combine         */
   MOE_STAGE_FINALIZE = 6,  /* round the accumulator to the output type           */
   MOE_STAGE_COUNT = 7

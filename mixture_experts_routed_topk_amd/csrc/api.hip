@@ -137,7 +137,7 @@ Plan make_plan(const moe_problem& p) {
 struct Layout {
   size_t bad, counts, offsets, mt, perm, inv;
   size_t route_part; // chunked routing: per-chunk expert counts [G][E] and bad-id counts [G]
-  size_t act;        // SwiGLU rows [A][I]: f32 (f32 weights, and fp8 before quantising) or bf16
+  size_t act;        // SwiGLU rows [A][I]: f32 (f32 weights) or bf16 (bf16 weights); none for fp8 / fp4
   size_t act_q;      // fp8 / fp4: e4m3 SwiGLU rows [A][I]
   size_t act_s;      // fp8 / fp4: their scales [A][I/128]
   size_t x_q, x_s;   // fp8 / fp4: e4m3 hidden rows [T][H] and scales [T][H/128]
@@ -163,7 +163,8 @@ Layout make_layout(const moe_problem& p) {
   L.inv = take(4 * A);
   L.route_part = take(4 * (E + 1) * (size_t)kRouteMaxChunks);
   const bool fp8 = quant_acts(p);
-  L.act = take((p.weight_dtype == MOE_BF16 ? 2 : 4) * A * I);
+  // (fp8 / fp4: the gate_up kernels write e4m3 codes and scales only, no float rows)
+  L.act = fp8 ? o : take((p.weight_dtype == MOE_BF16 ? 2 : 4) * A * I);
   L.act_q = fp8 ? take(A * I) : o;
   L.act_s = fp8 ? take(4 * A * (I / 128)) : o;
   L.x_q = fp8 ? take(T * H) : o;
@@ -269,10 +270,12 @@ moe_status moe_plan_describe(const moe_problem* p, char* buf, size_t len) {
                      : is_fp4(*p) ? "mfma16x16x128_e4m3xe2m1_scaled_128x256_ring3"
                                   : "mfma16x16x128_e4m3_scaled_128x256_ring3";
   const char* gname = (p->flags & MOE_FLAG_ACT_GELU) ? "geglu" : ((p->flags & MOE_FLAG_ACT_RELU) ? "reglu" : "swiglu");
-  snprintf(buf, len, "path=%s weights=%s scales=%s kernels=%s activation=%s combine=%s workspace_bytes=%zu",
-           pl.path == kDecode ? "decode" : "grouped", wname, sname, kern, gname,
-           slot_combine(*p) ? (slot_rows_bf16(*p, pl.path == kDecode) ? "slot_rows_bf16" : "slot_rows_f32")
-                            : "atomic_f32", L.total);
+  const int n = snprintf(buf, len, "path=%s weights=%s scales=%s kernels=%s activation=%s combine=%s workspace_bytes=%zu",
+                         pl.path == kDecode ? "decode" : "grouped", wname, sname, kern, gname,
+                         slot_combine(*p) ? (slot_rows_bf16(*p, pl.path == kDecode) ? "slot_rows_bf16" : "slot_rows_f32")
+                                          : "atomic_f32", L.total);
+  if (quant_acts(*p) && n > 0 && (size_t)n < len)
+    snprintf(buf + n, len - n, " act_codes_offset=%zu act_scales_offset=%zu", L.act_q, L.act_s);
   return MOE_OK;
 }
 
@@ -446,7 +449,8 @@ moe_status moe_experts_forward(const moe_problem* p, const void* hidden, const i
   gu.b_rows = 2 * p->I;
   gu.b_expert_stride = 2 * (int64_t)p->I * p->H / (fp4 ? 2 : 1);   // (fp4: bytes)
   gu.K = p->H;
-  gu.act_out = ws + L.act;
+  gu.act_out = fp8 ? (void*)(ws + L.act_q) : (void*)(ws + L.act);
+  gu.act_scale_out = fp8 ? reinterpret_cast<float*>(ws + L.act_s) : nullptr;
   if (zero_in_gateup) {
     gu.zero_out = acc;
     gu.zero_n4 = p->T * (int64_t)p->H / 4;   // H is a multiple of 128
@@ -503,14 +507,7 @@ moe_status moe_experts_forward(const moe_problem* p, const void* hidden, const i
     const int gu_grid = persistent_grid(dev->cus, 1, max_mtiles(A, p->E, pl.bm) * gu.NT);
     MOE_HIP_CHECK(fp4 ? launch_gateup_fp4(gu, gu_grid, s)
                       : (fp8 ? launch_gateup_fp8(gu, gu_grid, s) : launch_gateup_bf16(gu, gu_grid, s)));
-    MOE_HIP_CHECK(stage_mark(MOE_STAGE_GATE_UP, 1, s));
-    if (fp8) {
-      MOE_HIP_CHECK(stage_mark(MOE_STAGE_QUANT_ACT, 0, s));
-      MOE_HIP_CHECK(launch_quant_rows_f32(reinterpret_cast<const float*>(ws + L.act), A, p->I,
-                                          reinterpret_cast<uint8_t*>(ws + L.act_q),
-                                          reinterpret_cast<float*>(ws + L.act_s), s));
-      MOE_HIP_CHECK(stage_mark(MOE_STAGE_QUANT_ACT, 1, s));
-    }
+    MOE_HIP_CHECK(stage_mark(MOE_STAGE_GATE_UP, 1, s));   // (fp8 / fp4: a quantised in its epilogue)
     MOE_HIP_CHECK(stage_mark(MOE_STAGE_DOWN, 0, s));
     const int dn_grid = persistent_grid(dev->cus, 1, max_mtiles(A, p->E, pl.bm) * dn.NT);
     MOE_HIP_CHECK(fp4 ? launch_down_fp4(dn, dn_grid, s)
@@ -556,6 +553,18 @@ moe_status moe_quantize_rows_fp8(const void* x_bf16, int64_t rows, int32_t cols,
   if (!aligned16(x_bf16) || (reinterpret_cast<uintptr_t>(q) & 7u) || !aligned4(scales)) return MOE_ERR_BAD_SHAPE;
   (void)hipGetLastError();  // see moe_experts_forward
   MOE_HIP_CHECK(launch_quant_rows_bf16(x_bf16, rows, cols, q, scales, static_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
+moe_status moe_check_mfma_blocks(int fmt, const uint8_t* a, const uint8_t* b, const uint8_t* b_scale, float* d,
+                                 int nblocks, void* stream) {
+  if (fmt != 0 && fmt != 1) return MOE_ERR_UNSUPPORTED;
+  if (nblocks < 0) return MOE_ERR_BAD_SHAPE;
+  if (nblocks == 0) return MOE_OK;
+  if (!a || !b || !d || (fmt == 1 && !b_scale)) return MOE_ERR_NULL_ARG;
+  if (!aligned16(a) || !aligned16(b) || !aligned4(d)) return MOE_ERR_BAD_SHAPE;
+  (void)hipGetLastError();  // see moe_experts_forward
+  MOE_HIP_CHECK(launch_mfma_block_check(a, b, b_scale, d, nblocks, fmt, static_cast<hipStream_t>(stream)));
   return MOE_OK;
 }
 

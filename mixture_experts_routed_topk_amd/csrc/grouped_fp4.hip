@@ -11,8 +11,9 @@
 // accumulator times the row scale sa.
 //
 // gate_up: a tile's 256 weight rows are 128 gate rows and the matching 128 up rows, so the
-// epilogue forms gate(g) * u for 128 SwiGLU columns in registers and writes it as float32
-// (requantised to e4m3 by the row quantiser before the down projection).  down: 256 output
+// epilogue forms gate(g) * u for 128 SwiGLU columns in registers -- one activation scale
+// group per row -- and writes them as e4m3 codes with their per-row float32 scale
+// (act_quant_epilogue.h).  down: 256 output
 // columns; the epilogue multiplies by the routing weight and adds the row into the token's
 // float32 output row (hardware float atomics) or stores it to the slot's own row.
 //
@@ -27,6 +28,7 @@
 // over its M tiles (multiples of 32 rows); persistent grid with XCD-contiguous runs of items.
 #include <type_traits>
 
+#include "act_quant_epilogue.h"
 #include "device_common.h"
 #include "internal.h"
 
@@ -53,6 +55,7 @@ constexpr int ALD = BM / ARPI / NW;        // A DMA instructions per wave per sl
 constexpr int BLD = BN / BRPI / NW;        // B DMA instructions per wave per slice (2)
 constexpr int kMaxE = 1024;
 static_assert(ALD == 2 && BLD == 2, "the DMA of a slice is issued in parts 0 .. 2");
+static_assert(BM == kActQRows && BN / 2 == kActQCols && NSTAGE * STAGE >= kActQLdsBytes, "epilogue tile");
 
 enum { kGateUp = 0, kDownAtomic = 1, kDownSlots = 2 };
 
@@ -227,12 +230,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_fp4_kernel(GroupedArgs g)
           const i32x4 hi = *reinterpret_cast<const i32x4*>(ap + foff1);
           const i32x8 af = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           const f32x4 sa = *reinterpret_cast<const f32x4*>(&Sa[(2 * i + wm) * 16 + 4 * g4]);
+          // four independent block products first, then their folds (the MFMAs write
+          // distinct registers and issue back to back)
+          f32x4 pr[NFRAG];
 #pragma unroll
-          for (int j = 0; j < NFRAG; ++j) {
-            const f32x4 pr = mfma_16x16x128_e4m3_e2m1(af, bf[j], sbv[j]);
+          for (int j = 0; j < NFRAG; ++j) pr[j] = mfma_16x16x128_e4m3_e2m1(af, bf[j], sbv[j]);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc[i][j][q] = fmaf(pr[q], sa[q], acc[i][j][q]);
-          }
+          for (int j = 0; j < NFRAG; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[i][j][q] = fmaf(pr[j][q], sa[q], acc[i][j][q]);
         }
         if (next && i < 3) issue_part(kt + 2, nslot, i);
       }
@@ -261,22 +267,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_fp4_kernel(GroupedArgs g)
     // 16x16 fragment (i, j): element q at tile row (2 i + wm) * 16 + 4 g4 + q, tile column
     // bcol0(j) + l16
     if constexpr (MODE == kGateUp) {
-      float* out = static_cast<float*>(g.act_out);
-#pragma unroll
-      for (int i = 0; i < MFRAG; ++i) {
-        if ((2 * i + wm) * 16 >= rows) break;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int r = (2 * i + wm) * 16 + 4 * g4 + q;
-          if (r >= rows) continue;
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int col = nt * (BN / 2) + 32 * wn + 16 * j + l16;
-            if (col < ncols)
-              out[(int64_t)(row0 + r) * g.I + col] = gate_fn<false>(g.gate, acc[i][j][q]) * acc[i][j + 2][q];
-          }
-        }
-      }
+      __syncthreads();   // every wave is done with the ring
+      gateup_requant_epilogue<MFRAG>(acc, g.gate, wm, wn, l16, g4, tid, rows, row0, nt, g.I, &ring[0][0],
+                                     static_cast<uint8_t*>(g.act_out), g.act_scale_out);
     } else {
       if (tid < BM) {
         sTok[tid] = my_tok;

@@ -11,8 +11,9 @@
 // float32 accumulator times the two scales.
 //
 // gate_up: a tile's 256 weight rows are 128 gate rows and the matching 128 up rows, so the
-// epilogue forms gate(g) * u for 128 SwiGLU columns in registers and writes it as float32
-// (requantised to e4m3 by the row quantiser before the down projection).  down: 256 output
+// epilogue forms gate(g) * u for 128 SwiGLU columns in registers -- one activation scale
+// group per row -- and writes them as e4m3 codes with their per-row float32 scale, ready
+// for the down projection (act_quant_epilogue.h).  down: 256 output
 // columns; the epilogue multiplies by the routing weight and adds the row into the token's
 // float32 output row (hardware float atomics) or stores it to the slot's own row
 // (per-slot combine).
@@ -29,6 +30,7 @@
 // of 32 rows, at most 128); persistent grid with XCD-contiguous runs of items.
 #include <type_traits>
 
+#include "act_quant_epilogue.h"
 #include "device_common.h"
 #include "internal.h"
 
@@ -52,6 +54,7 @@ constexpr int BLD = BN / RPI / NW;         // B DMA instructions per wave per sl
 constexpr int kMaxE = 1024;
 constexpr int kMaxKB = 512;                // K / 128 (K = I <= 65536)
 static_assert(ALD <= 4 && BLD == 4, "the DMA of a slice is spread over four parts");
+static_assert(BM == kActQRows && BN / 2 == kActQCols && NSTAGE * STAGE >= kActQLdsBytes, "epilogue tile");
 
 enum { kGateUp = 0, kDownAtomic = 1, kDownSlots = 2 };
 
@@ -246,12 +249,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_fp8_kernel(GroupedArgs g)
             s0[q] = sa[q] * sb0;
             s1[q] = sa[q] * sb1;
           }
+          // four independent block products first, then their folds: each MFMA writes its
+          // own registers, so the next one issues without waiting for the previous fold
+          f32x4 pr[NFRAG];
 #pragma unroll
-          for (int j = 0; j < NFRAG; ++j) {
-            const f32x4 pr = mfma_16x16x128_e4m3(af, bf[j], f32x4{});
+          for (int j = 0; j < NFRAG; ++j) pr[j] = mfma_16x16x128_e4m3(af, bf[j], f32x4{});
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc[i][j][q] = fmaf(pr[q], j < 2 ? s0[q] : s1[q], acc[i][j][q]);
-          }
+          for (int j = 0; j < NFRAG; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[i][j][q] = fmaf(pr[j][q], j < 2 ? s0[q] : s1[q], acc[i][j][q]);
         }
         if (next) issue_part(kt + 2, nslot, i);
       }
@@ -281,22 +287,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_fp8_kernel(GroupedArgs g)
     // 16x16 fragment (i, j): element q at tile row (2 i + wm) * 16 + 4 g4 + q, tile column
     // bcol0(j) + l16
     if constexpr (MODE == kGateUp) {
-      float* out = static_cast<float*>(g.act_out);
-#pragma unroll
-      for (int i = 0; i < MFRAG; ++i) {
-        if ((2 * i + wm) * 16 >= rows) break;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int r = (2 * i + wm) * 16 + 4 * g4 + q;
-          if (r >= rows) continue;
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int col = nt * (BN / 2) + 32 * wn + 16 * j + l16;
-            if (col < ncols)
-              out[(int64_t)(row0 + r) * g.I + col] = gate_fn<false>(g.gate, acc[i][j][q]) * acc[i][j + 2][q];
-          }
-        }
-      }
+      __syncthreads();   // every wave is done with the ring
+      gateup_requant_epilogue<MFRAG>(acc, g.gate, wm, wn, l16, g4, tid, rows, row0, nt, g.I, &ring[0][0],
+                                     static_cast<uint8_t*>(g.act_out), g.act_scale_out);
     } else {
       if (tid < BM) {
         sTok[tid] = my_tok;

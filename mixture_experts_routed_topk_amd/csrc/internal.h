@@ -62,7 +62,8 @@ struct GroupedArgs {
   const int32_t* mt;        // [E+1] M-tile starts for this GEMM's tile height
   // gate_up epilogue
   int I;                    // intermediate size (up rows start at I)
-  void* act_out;            // [A][I] SwiGLU output (bf16 / f32)
+  void* act_out;            // [A][I] SwiGLU output: bf16 / f32, or e4m3 codes (fp8, fp4)
+  float* act_scale_out;     // fp8, fp4: [A][I/128] float32 scales of the e4m3 codes
   // down epilogue
   const int32_t* perm;      // sorted position -> slot
   const float* topk_w;      // [A] routing weights by slot
@@ -132,8 +133,12 @@ hipError_t launch_decode_down(const GroupedArgs& g, int grid, hipStream_t s);
 // Per-row, per-128-column e4m3 quantisation: scale = amax/448 (1 if amax == 0).
 hipError_t launch_quant_rows_bf16(const void* x, int64_t rows, int cols, uint8_t* q, float* scales,
                                   hipStream_t s);
-hipError_t launch_quant_rows_f32(const float* x, int64_t rows, int cols, uint8_t* q, float* scales,
-                                 hipStream_t s);
+
+// ---------------------------------------------------------------------------- instruction check
+// nblocks independent 16x16x128 block products on the block-scaled MFMA (fmt 0: e4m3 x e4m3,
+// fmt 1: e4m3 x e2m1 with per-32 UE8M0 exponents), zero accumulator, one wave per block.
+hipError_t launch_mfma_block_check(const uint8_t* a, const uint8_t* b, const uint8_t* b_scale, float* d, int nblocks,
+                                   int fmt, hipStream_t s);
 
 // ---------------------------------------------------------------------------- elementwise
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);

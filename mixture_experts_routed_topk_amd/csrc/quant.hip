@@ -1,4 +1,5 @@
-// Dynamic per-row e4m3 quantisation of activations (fp8 experts).
+// Dynamic per-row e4m3 quantisation of the hidden states (fp8 and fp4 experts; the SwiGLU
+// rows are quantised the same way inside the gate_up kernels, act_quant_epilogue.h).
 //
 // The Experts backends page ("FP8 and FP4 quantized experts" section) requires
 // dynamic activation scales per row and rejects static per-tensor scales.  Here each
@@ -18,7 +19,6 @@ namespace {
 
 constexpr int kThreads = 256;
 
-template <bool BF16_IN>
 __global__ __launch_bounds__(kThreads) void quant_rows_kernel(const void* __restrict__ x, int64_t groups, int cols,
                                                               uint8_t* __restrict__ q, float* __restrict__ scales) {
   const int sub = threadIdx.x & 15;                       // lane within the group
@@ -31,21 +31,11 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(const void* __rest
     const int64_t col = (grp - row * gpr) * 128 + sub * 8;
     const int64_t at = row * cols + col;
     float v[8];
-    if (BF16_IN) {
-      const i32x4 raw = *reinterpret_cast<const i32x4*>(static_cast<const uint16_t*>(x) + at);
+    const i32x4 raw = *reinterpret_cast<const i32x4*>(static_cast<const uint16_t*>(x) + at);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[2 * i] = bf16_lo((uint32_t)raw[i]);
-        v[2 * i + 1] = bf16_hi((uint32_t)raw[i]);
-      }
-    } else {
-      const f32x4 a = *reinterpret_cast<const f32x4*>(static_cast<const float*>(x) + at);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(static_cast<const float*>(x) + at + 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[i] = a[i];
-        v[4 + i] = b[i];
-      }
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_lo((uint32_t)raw[i]);
+      v[2 * i + 1] = bf16_hi((uint32_t)raw[i]);
     }
     float amax = 0.f;
 #pragma unroll
@@ -73,14 +63,7 @@ int grid_for(int64_t groups) {
 
 hipError_t launch_quant_rows_bf16(const void* x, int64_t rows, int cols, uint8_t* q, float* scales, hipStream_t s) {
   const int64_t groups = rows * (cols / 128);
-  hipLaunchKernelGGL(quant_rows_kernel<true>, dim3(grid_for(groups)), dim3(kThreads), 0, s, x, groups, cols, q,
-                     scales);
-  return hipGetLastError();
-}
-
-hipError_t launch_quant_rows_f32(const float* x, int64_t rows, int cols, uint8_t* q, float* scales, hipStream_t s) {
-  const int64_t groups = rows * (cols / 128);
-  hipLaunchKernelGGL(quant_rows_kernel<false>, dim3(grid_for(groups)), dim3(kThreads), 0, s, x, groups, cols, q,
+  hipLaunchKernelGGL(quant_rows_kernel, dim3(grid_for(groups)), dim3(kThreads), 0, s, x, groups, cols, q,
                      scales);
   return hipGetLastError();
 }

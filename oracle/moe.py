@@ -262,13 +262,20 @@ def _prepare_x(x: np.ndarray, act: str, fp8: bool) -> np.ndarray:
     return xf
 
 
-def _swiglu_then_requant(gu: np.ndarray, I: int, fp8: bool, gate: str = "silu") -> np.ndarray:
+def _swiglu_then_requant(gu: np.ndarray, I: int, fp8: bool, gate: str = "silu", parts=None) -> np.ndarray:
     """gu [..., 2I] fp64 -> the activation fed to the down projection: gate(g) * u with the
-    gate function silu (SwiGLU, the default), gelu (GeGLU) or relu (ReGLU)."""
+    gate function silu (SwiGLU, the default), gelu (GeGLU) or relu (ReGLU).
+
+    With e4m3 activations the result, rounded to fp32, is quantised per row and 128 columns
+    and dequantised.  If `parts` is a list, (gu, a rounded to fp32, codes, scales) of these
+    rows is appended to it (the intermediate values, for inspection; nothing else changes).
+    """
     a = GATES[gate](gu[..., :I]) * gu[..., I:]
     if fp8:
         a2 = np.atleast_2d(f64_to_f32(a))
         q, s = quant_rows(a2)
+        if parts is not None:
+            parts.append((np.atleast_2d(gu), a2, q, s))
         a = dequant_rows(q, s).reshape(a.shape)
     return a
 
@@ -284,7 +291,8 @@ def out_as_f64(out: np.ndarray, act: str) -> np.ndarray:
 
 def forward(x: np.ndarray, idx: np.ndarray, w: np.ndarray, weights: ExpertWeights, *,
             act: str, E: Optional[int] = None, mode: str = "fast",
-            tokens: Optional[Sequence[int]] = None, gate: str = "silu"):
+            tokens: Optional[Sequence[int]] = None, gate: str = "silu",
+            capture: Optional[dict] = None):
     """Routed top-k experts forward.
 
     x: [T, H] (fp32 values or bf16 bits); idx: int [T, k]; w: float32 [T, k].
@@ -292,6 +300,9 @@ def forward(x: np.ndarray, idx: np.ndarray, w: np.ndarray, weights: ExpertWeight
     tokens: optional subset of token rows to evaluate (each token is independent).
     gate: the gated activation, "silu" (SwiGLU), "gelu" (GeGLU, exact erf form) or "relu"
     (ReGLU).
+    capture: with e4m3 activations (fp8 / fp4 experts), an optional dict that receives, for
+    every evaluated slot (token t, slot j), capture[(t, j)] = (gu fp64 [2I], a as fp32 [I],
+    e4m3 codes [I], float32 scales [I/128]): the SwiGLU intermediates of the definition.
     Returns (acc fp64 [n, H], out [n, H] in the output storage) for the chosen
     rows (all T rows when tokens is None), in the order of `tokens`.
     """
@@ -319,7 +330,11 @@ def forward(x: np.ndarray, idx: np.ndarray, w: np.ndarray, weights: ExpertWeight
                     cache[e] = (weights.gate_up_f64(e), weights.down_f64(e))
                 wgu, wd = cache[e]
                 I = wd.shape[1]
-                a = _swiglu_then_requant(wgu @ xs[r], I, fp8, gate)
+                parts = [] if (capture is not None and fp8) else None
+                a = _swiglu_then_requant(wgu @ xs[r], I, fp8, gate, parts)
+                if parts:
+                    gu_, a32_, q_, s_ = parts[0]
+                    capture[(int(rows[r]), j)] = (gu_[0], a32_[0], q_[0], s_[0])
                 acc[r] += ws[r, j] * (wd @ a)
     elif mode == "fast":
         flat = ids.reshape(-1)
@@ -328,7 +343,12 @@ def forward(x: np.ndarray, idx: np.ndarray, w: np.ndarray, weights: ExpertWeight
             r_of, j_of = sl // k, sl % k
             wgu, wd = weights.gate_up_f64(int(e)), weights.down_f64(int(e))
             I = wd.shape[1]
-            a = _swiglu_then_requant(xs[r_of] @ wgu.T, I, fp8, gate)
+            parts = [] if (capture is not None and fp8) else None
+            a = _swiglu_then_requant(xs[r_of] @ wgu.T, I, fp8, gate, parts)
+            if parts:
+                gu_, a32_, q_, s_ = parts[0]
+                for n_, (r_, j_) in enumerate(zip(r_of, j_of)):
+                    capture[(int(rows[r_]), int(j_))] = (gu_[n_], a32_[n_], q_[n_], s_[n_])
             y = a @ wd.T
             np.add.at(acc, r_of, ws[r_of, j_of][:, None] * y)
     else:
