@@ -3,13 +3,18 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
 
-One step is one full forward -- routing bookkeeping, (fp8: activation
+One step is one full forward -- routing bookkeeping, (fp8/fp4: activation
 quantisation,) gate/up GEMM + SwiGLU, down GEMM + weighted combine, finalize --
 over one batch of seeded synthetic inputs already resident in HBM.  The default
-workload is the Qwen1.5-MoE-A2.7B-shaped bf16 prefill layer (T=4096, H=2048,
-I=1408, E=60, top-4).  Prints one JSON line: whole-job tokens/s, the dominant
-kernel's roofline figures (its launches timed with HIP events on the library's
-stream inside the timed region), and the CPU oracle timed on a bounded sample.
+workload is the DeepSeek-V3-shaped bf16 prefill layer (T=8192, H=7168, I=2048,
+E=256, top-8, Zipf-skewed routing), the largest layer of the set that fits one GPU.
+Each timed forward is bracketed by HIP events on the library's stream, and 1 GiB of
+scratch is written between forwards (outside the events) so that no step starts with
+the previous step's data in the 256 MB Infinity Cache.  Prints one JSON line:
+tokens/s from the median step, the step's median/min/max, the dominant kernel's
+roofline figures (its launches bracketed by HIP events in every timed step), and
+the CPU oracle timed on bounded samples (expert-major fp64 BLAS over all host
+cores, and the per-token loop).
 """
 
 from __future__ import annotations
@@ -221,46 +226,94 @@ def copy_calibration(nbytes: int = 256 << 20, reps: int = 3):
                                            "launches": reps}}), flush=True)
 
 
+def _blas_info():
+    try:
+        from threadpoolctl import threadpool_info
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"] or threadpool_info()
+        return (info[0].get("internal_api", "?"), int(max(i.get("num_threads", 1) for i in info))) if info else ("?", 1)
+    except Exception:  # pragma: no cover
+        return "?", 1
+
+
 def cpu_baseline(spec, D, seconds: float):
-    """The fp64 oracle (per-token loop over the k chosen experts) on a token sample."""
+    """The fp64 oracle timed on bounded samples of the same layer, weight generation excluded.
+
+    fast: the oracle's expert-major mode (fp64 BLAS over all host cores) on the first n tokens,
+    n doubled from 8 while the run stays short; the largest sample is reported.
+    literal: the per-token loop over the k chosen experts on the first tokens, about a third
+    of the time budget.
+    """
     import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
     import synth
     from oracle.moe import ExpertWeights, forward
 
     cache = {}
 
-    def get(which, e):
-        key = (which, e)
-        if key not in cache:
-            cache[key] = (synth.expert_gate_up if which == 0 else synth.expert_down)(spec, e)
-        return cache[key]
+    def gen(e):
+        return e, synth.expert_gate_up(spec, e), synth.expert_down(spec, e)
+
+    def prefetch(experts):
+        todo = [int(e) for e in experts if int(e) not in cache]
+        with ThreadPoolExecutor(max_workers=16) as ex:
+            for e, g, d in ex.map(gen, todo):
+                cache[e] = (g, d)
 
     if spec.weight in ("fp8", "fp4"):
-        W = ExpertWeights(spec.weight, lambda e: get(0, e)[0], lambda e: get(1, e)[0], spec.scale,
-                          lambda e: get(0, e)[1], lambda e: get(1, e)[1])
+        W = ExpertWeights(spec.weight, lambda e: cache[e][0][0], lambda e: cache[e][1][0], spec.scale,
+                          lambda e: cache[e][0][1], lambda e: cache[e][1][1])
     else:
-        W = ExpertWeights(spec.weight, lambda e: get(0, e), lambda e: get(1, e))
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
-    # warm the weight cache for the first tokens so generation is not timed
-    n_done, t_oracle = 0, 0.0
-    t = 0
-    while t_oracle < seconds and t < spec.T:
-        for e in set(int(v) for v in D["idx_host"][t]):
-            get(0, e), get(1, e)
+        W = ExpertWeights(spec.weight, lambda e: cache[e][0], lambda e: cache[e][1])
+    vendor, threads = _blas_info()
+    idx = D["idx_host"]
+    # fast mode on growing token prefixes: most of a small sample's time is converting the
+    # experts it touches, so the next sample's time is extrapolated linearly in n
+    budget = 2 * seconds / 3
+    n, hist, spent = min(spec.T, 256), [], 0.0
+    while True:
+        toks = np.arange(n)
+        prefetch(np.unique(idx[toks]))
         t0 = time.perf_counter()
-        forward(D["x_host"], D["idx_host"], D["w_host"], W, act=spec.act, E=spec.E,
-                mode="literal", tokens=[t])
-        t_oracle += time.perf_counter() - t0
-        n_done += 1
-        t += 1
-    return {"value": n_done / t_oracle, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {n_done} tokens of the same layer, fp64 per-token loop over the k "
-                      f"chosen experts (literal mode), {t_oracle:.1f} s of CPU time",
-            "host_cpus": len(os.sched_getaffinity(0))}
+        forward(D["x_host"], idx, D["w_host"], W, act=spec.act, E=spec.E, mode="fast", tokens=toks)
+        dt = time.perf_counter() - t0
+        spent += dt
+        hist.append((n, dt))
+        if n == spec.T:
+            break
+        nxt = min(2 * n, spec.T)
+        if len(hist) > 1:
+            (n0, d0), (n1, d1) = hist[-2], hist[-1]
+            pred = d1 + max(d1 - d0, 0.0) * (nxt - n1) / (n1 - n0)
+        else:
+            pred = 2 * dt
+        if spent + pred > budget:
+            break
+        n = nxt
+    fast = hist[-1]
+    # literal mode on the first tokens, one BLAS thread
+    from threadpoolctl import threadpool_limits
+    t_lit, n_lit, t = 0.0, 0, 0
+    with threadpool_limits(1):
+        while t_lit < seconds / 3 and t < spec.T:
+            prefetch(np.unique(idx[t]))
+            t0 = time.perf_counter()
+            forward(D["x_host"], idx, D["w_host"], W, act=spec.act, E=spec.E, mode="literal", tokens=[t])
+            t_lit += time.perf_counter() - t0
+            n_lit += 1
+            t += 1
+    n_f, t_f = fast
+    return {"value": n_f / t_f, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n_f} tokens of the same layer, fp64 oracle in its expert-major mode ({vendor} BLAS, "
+                      f"{threads} threads), {t_f:.1f} s; weight generation not timed",
+            "blas": vendor, "host_cpus": len(os.sched_getaffinity(0)),
+            "literal": {"value": n_lit / t_lit, "unit": "tokens/s", "cores": 1,
+                        "sample": f"first {n_lit} tokens, per-token fp64 loop over the k chosen experts, "
+                                  f"{t_lit:.1f} s"}}
+
+
+def _stats(v):
+    v = sorted(v)
+    return {"median": v[len(v) // 2], "min": v[0], "max": v[-1], "mean": sum(v) / len(v), "n": len(v)}
 
 
 def main():
@@ -270,9 +323,14 @@ def main():
     # the first 50 steps after 10 warm-up steps ran 9% slower than every later 50)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--config", default="qwen_prefill_bf16", choices=sorted(WORKLOADS))
+    ap.add_argument("--config", default="dsv3_prefill_bf16", choices=sorted(WORKLOADS))
     ap.add_argument("--flags", type=int, default=0, help="MOE_FLAG_* bits passed to the forward")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=30.0)
+    ap.add_argument("--flush-mib", type=int, default=1024,
+                    help="MiB of scratch touched between timed steps (outside the step events)")
+    ap.add_argument("--flush", choices=("write", "read", "none"), default="write",
+                    help="how the scratch evicts the caches: written (leaves dirty lines the next "
+                         "step writes back), read (clean lines), or not at all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 256 MiB device copy (counter calibration for the traffic figure)")
@@ -336,24 +394,40 @@ def main():
     dominant = max(("gate_up", "down"), key=lambda n: stage_ms.get(n, 0.0))
     dom = m.STAGES.index(dominant)
 
-    # timed region: only the dominant kernel is bracketed by events
+    # timed region: every forward bracketed by step events, the dominant kernel by stage
+    # events; a scratch write between forwards (outside the step events) evicts the cache
+    flush = torch.zeros(max(args.flush_mib, 1) << 20, dtype=torch.uint8, device=dev)
     tev = hev.create(2 * args.steps)
+    sev = hev.create(2 * args.steps)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    rec = hev.hip.hipEventRecord
+    rec.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     handles = [None] * (2 * nst)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        if args.flush == "write":
+            flush.fill_(i & 0xFF)
+        elif args.flush == "read":
+            torch.amax(flush)
         handles[2 * dom], handles[2 * dom + 1] = tev[2 * i], tev[2 * i + 1]
         m.set_stage_events(handles)
+        rec(ctypes.c_void_p(sev[2 * i]), stream)
         step()
+        rec(ctypes.c_void_p(sev[2 * i + 1]), stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     m.set_stage_events(None)
     kern_ms = [hev.elapsed_ms(tev[2 * i], tev[2 * i + 1]) for i in range(args.steps)]
+    step_ms = [hev.elapsed_ms(sev[2 * i], sev[2 * i + 1]) for i in range(args.steps)]
     hev.destroy(tev)
+    hev.destroy(sev)
+    del flush
 
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    tokens_per_s = spec.T * args.steps / (t1 - t0)
-    kavg = sum(kern_ms) / len(kern_ms)
+    step_st, kern_st = _stats(step_ms), _stats(kern_ms)
+    ms_per_step = step_st["median"]
+    tokens_per_s = spec.T / (ms_per_step * 1e-3)
+    kavg = kern_st["mean"]
     flops, byts = algorithmic(spec, n_active, dominant)
     peak_f = PEAK_TFLOPS[spec.weight]
     t_mfma = flops / (peak_f * 1e12)
@@ -365,7 +439,9 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     kname, digest = kernel_digest(plan.split()[0].split("=")[1], spec.weight, dominant)
     roof["traffic"] = recorded_traffic(kname, dominant, args.config, digest)
-    roof.update({"kernel": f"{kname}:{dominant}", "kernel_source_sha256": digest, "avg_ms": kavg, "launches": len(kern_ms),
+    roof.update({"kernel": f"{kname}:{dominant}", "kernel_source_sha256": digest, "avg_ms": kavg,
+                 "median_ms": kern_st["median"], "min_ms": kern_st["min"], "max_ms": kern_st["max"],
+                 "launches": len(kern_ms),
                  "algorithmic_flops": flops, "algorithmic_bytes": byts,
                  "mfma_frac": flops / (kavg * 1e-3) / 1e12 / peak_f,
                  "hbm_frac": byts / (kavg * 1e-3) / 1e9 / PEAK_HBM_GBS})
@@ -379,6 +455,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "step_ms": {k: step_st[k] for k in ("median", "min", "max", "mean")},
+        "ms_per_step_wall": (t1 - t0) * 1e3 / args.steps,
+        "cache_flush": {"mib": args.flush_mib if args.flush != "none" else 0, "mode": args.flush},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -39,7 +39,16 @@ def test_traffic_record_matches_current_sources(fname):
     assert bench.recorded_traffic(name, stage, config, digest) == float(rec["traffic_bytes_per_launch"])
 
 
-def test_default_workload_algorithmic_counts():
+def test_default_workload_is_the_largest_single_gpu_layer():
+    import argparse
+    assert bench.WORKLOADS["dsv3_prefill_bf16"].startswith("DeepSeek-V3-shaped bf16 prefill")
+    spec = synth.spec_for("dsv3_prefill_bf16")
+    flops, byts = bench.algorithmic(spec, 187, "gate_up")
+    assert flops == 4.0 * 65536 * 7168 * 2048                      # 3.85 TFLOP
+    assert byts == 187 * 2 * 2048 * 7168 * 2 + 8192 * 7168 * 2 + 65536 * 2048 * 2
+
+
+def test_qwen_prefill_algorithmic_counts():
     spec = synth.spec_for("qwen_prefill_bf16")
     flops, byts = bench.algorithmic(spec, 60, "gate_up")
     assert flops == 4.0 * 16384 * 2048 * 1408                      # 189.0 GFLOP
