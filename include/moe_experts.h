@@ -181,6 +181,30 @@ moe_status moe_experts_forward(const moe_problem* p, const void* hidden, const i
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The forward without a workspace argument and without any allocation, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results and errors as
+ * moe_experts_forward, minus workspace and workspace_bytes: the workspace is a device
+ * array inside the library of moe_noalloc_scratch_bytes() bytes (128 MiB), one copy per
+ * GPU, held until the process ends (looked up once per device on its first call).
+ * Problems whose moe_workspace_size exceeds it return MOE_ERR_WORKSPACE_TOO_SMALL before
+ * any HIP call (the Qwen1.5-MoE-A2.7B-shaped prefill layer, T = 4096, needs 108 MiB; the
+ * DeepSeek-V3-shaped layers need more: use moe_experts_forward for them).  The call makes
+ * no hipMalloc, hipFree or other allocation.  Every call on one GPU uses that GPU's one
+ * array: calls that overlap on one GPU (on different streams, or from different host
+ * threads without ordering) race and may produce wrong results; calls ordered on one
+ * stream are safe.  The array keeps the last call's contents; nothing the forward reads
+ * from it needs to start at zero.
+ */
+moe_status moe_experts_forward_noalloc(const moe_problem* p, const void* hidden, const int32_t* topk_idx,
+                                       const float* topk_w, const void* w_gate_up, const void* w_down,
+                                       const void* w_gate_up_scale, const void* w_down_scale, void* out,
+                                       void* stream);
+
+/* Bytes of the allocation-free forward's device array (its largest workspace). */
+size_t moe_noalloc_scratch_bytes(void);
+
+/*
  * Routing bookkeeping alone: the stable sort of the T*k slots a = t*k + j by
  * chosen expert (page backend table, "grouped_mm" row: tokens are sorted by
  * their selected expert before one grouped GEMM).

@@ -16,7 +16,7 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "experts_forward", "check_scales", "check_mfma_blocks", "route", "route_logits", "quantize_rows_fp8", "workspace_size", "plan_describe",
+    "experts_forward", "experts_forward_noalloc", "check_scales", "check_mfma_blocks", "route", "route_logits", "quantize_rows_fp8", "workspace_size", "plan_describe",
     "Problem", "MoeError", "lib", "FLAG_CHECK_INDICES", "FLAG_DETERMINISTIC", "FLAG_ATOMIC_COMBINE", "FLAG_ACT_GELU", "FLAG_ACT_RELU",
     "FLAG_FORCE_GROUPED", "FLAG_FORCE_DECODE", "LIB_PATH",
 ]
@@ -40,7 +40,8 @@ FLAG_ACT_RELU = 64
 
 EXPORTS = ["moe_abi_version", "moe_status_str", "moe_workspace_size", "moe_experts_forward",
            "moe_route", "moe_route_logits", "moe_quantize_rows_fp8", "moe_plan_describe",
-           "moe_set_stage_events", "moe_check_mfma_blocks"]
+           "moe_set_stage_events", "moe_check_mfma_blocks", "moe_experts_forward_noalloc",
+           "moe_noalloc_scratch_bytes"]
 
 # stage ids (moe_set_stage_events)
 STAGES = ["zero", "route", "quant_x", "gate_up", "quant_act", "down", "finalize"]
@@ -81,6 +82,10 @@ def lib():
     L.moe_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
     L.moe_experts_forward.restype = ctypes.c_int
     L.moe_experts_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_experts_forward_noalloc.restype = ctypes.c_int
+    L.moe_experts_forward_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.moe_noalloc_scratch_bytes.restype = ctypes.c_size_t
+    L.moe_noalloc_scratch_bytes.argtypes = []
     L.moe_route.restype = ctypes.c_int
     L.moe_route.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_route_logits.restype = ctypes.c_int
@@ -241,6 +246,37 @@ def experts_forward(hidden: torch.Tensor, topk_idx: torch.Tensor, topk_w: torch.
         ctypes.byref(prob), _ptr(hidden), _ptr(topk_idx), _ptr(topk_w), _ptr(w_gate_up),
         _ptr(w_down), _ptr(w_gate_up_scale), _ptr(w_down_scale), _ptr(out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(hidden.device)))
+    return out
+
+
+def experts_forward_noalloc(hidden: torch.Tensor, topk_idx: torch.Tensor, topk_w: torch.Tensor,
+                            w_gate_up: torch.Tensor, w_down: torch.Tensor,
+                            w_gate_up_scale: Optional[torch.Tensor] = None,
+                            w_down_scale: Optional[torch.Tensor] = None,
+                            out: Optional[torch.Tensor] = None, flags: int = 0) -> torch.Tensor:
+    """experts_forward on the library's own device array instead of a workspace
+    (moe_experts_forward_noalloc): allocates nothing when `out` is given."""
+    for name, t in (("hidden", hidden), ("topk_idx", topk_idx), ("topk_w", topk_w),
+                    ("w_gate_up", w_gate_up), ("w_down", w_down)):
+        _need_gpu(name, t)
+    if topk_idx.dtype != torch.int32 or topk_w.dtype != torch.float32:
+        raise ValueError("topk_idx must be int32 and topk_w float32")
+    if topk_w.shape != topk_idx.shape:
+        raise ValueError("topk_w and topk_idx shapes differ")
+    prob = problem_for(hidden, topk_idx, w_gate_up, w_down, w_gate_up_scale, flags)
+    check_scales(prob, w_gate_up_scale, w_down_scale)
+    for name, t in (("w_gate_up_scale", w_gate_up_scale), ("w_down_scale", w_down_scale)):
+        if t is not None:
+            _need_gpu(name, t)
+    if out is None:
+        out = torch.empty_like(hidden)
+    else:
+        _need_gpu("out", out)
+        if out.shape != hidden.shape or out.dtype != hidden.dtype:
+            raise ValueError("out must match hidden in shape and dtype")
+    _check(lib().moe_experts_forward_noalloc(
+        ctypes.byref(prob), _ptr(hidden), _ptr(topk_idx), _ptr(topk_w), _ptr(w_gate_up), _ptr(w_down),
+        _ptr(w_gate_up_scale), _ptr(w_down_scale), _ptr(out), _stream(hidden.device)))
     return out
 
 

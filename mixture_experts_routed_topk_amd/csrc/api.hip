@@ -354,28 +354,38 @@ moe_status moe_route_logits(const moe_problem* p, const float* logits, int renor
   return MOE_OK;
 }
 
-moe_status moe_experts_forward(const moe_problem* p, const void* hidden, const int32_t* topk_idx, const float* topk_w,
-                               const void* w_gate_up, const void* w_down, const void* w_gate_up_scale,
-                               const void* w_down_scale, void* out, void* workspace, size_t workspace_bytes,
-                               void* stream) {
+}  // extern "C"
+
+namespace moe {
+namespace {
+
+// Host-side checks of a forward call that need no HIP call (workspace size aside).
+moe_status check_forward_args(const moe_problem* p, const void* hidden, const int32_t* topk_idx, const float* topk_w,
+                              const void* w_gate_up, const void* w_down, const void* w_gate_up_scale,
+                              const void* w_down_scale, const void* out) {
   moe_status st = validate_problem(p);
   if (st != MOE_OK) return st;
   if (p->T == 0) return MOE_OK;
-  if (!hidden || !topk_idx || !topk_w || !w_gate_up || !w_down || !out || !workspace) return MOE_ERR_NULL_ARG;
+  if (!hidden || !topk_idx || !topk_w || !w_gate_up || !w_down || !out) return MOE_ERR_NULL_ARG;
+  if (quant_acts(*p) && (!w_gate_up_scale || !w_down_scale)) return MOE_ERR_NULL_ARG;
+  if (!aligned16(hidden) || !aligned16(w_gate_up) || !aligned16(w_down) || !aligned16(out) || !aligned4(topk_idx) ||
+      !aligned4(topk_w) || !aligned4(w_gate_up_scale) || !aligned4(w_down_scale))
+    return MOE_ERR_BAD_SHAPE;
+  if ((p->flags & MOE_FLAG_FORCE_DECODE) && !decode_capable(*p)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// The forward's launches, arguments already checked (check_forward_args, T > 0) and the
+// workspace (16-byte aligned) holding at least make_layout(*p).total bytes.  Everything it
+// reads from the workspace is written first by its own kernels, so the workspace's
+// previous contents do not matter.
+moe_status forward_launch(const moe_problem* p, const void* hidden, const int32_t* topk_idx, const float* topk_w,
+                          const void* w_gate_up, const void* w_down, const void* w_gate_up_scale,
+                          const void* w_down_scale, void* out, void* workspace, DeviceRecord* dev, void* stream) {
   const bool fp8 = quant_acts(*p);     // e4m3 activation rows (fp8 and fp4 weights)
   const bool fp4 = is_fp4(*p);
-  if (fp8 && (!w_gate_up_scale || !w_down_scale)) return MOE_ERR_NULL_ARG;
-  if (!aligned16(hidden) || !aligned16(w_gate_up) || !aligned16(w_down) || !aligned16(out) ||
-      !aligned16(workspace) || !aligned4(topk_idx) || !aligned4(topk_w) || !aligned4(w_gate_up_scale) ||
-      !aligned4(w_down_scale))
-    return MOE_ERR_BAD_SHAPE;
   const Layout L = make_layout(*p);
-  if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
-  if ((p->flags & MOE_FLAG_FORCE_DECODE) && !decode_capable(*p)) return MOE_ERR_UNSUPPORTED;
   const Plan pl = make_plan(*p);
-
-  DeviceRecord* dev = nullptr;
-  if ((st = device_record(&dev)) != MOE_OK) return st;
   // launch errors are read with hipGetLastError(); drop an error left behind by an
   // earlier, unrelated HIP call on this thread so it is not reported as ours
   (void)hipGetLastError();
@@ -531,6 +541,75 @@ moe_status moe_experts_forward(const moe_problem* p, const void* hidden, const i
     if (nbad) return MOE_ERR_BAD_INDEX;
   }
   return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------- allocation-free forward
+// The workspace of moe_experts_forward_noalloc: a file-scope device array, one copy per GPU,
+// held for the life of the process.  Host code never passes the array's name to a kernel or
+// a copy (on the host it names a stand-in, not device memory); it uses the device address
+// that hipGetSymbolAddress returns, looked up once per device and kept in g_scratch.
+constexpr size_t kNoAllocScratchBytes = size_t(128) << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+struct ScratchRecord {
+  bool ready = false;
+  void* ptr = nullptr;
+};
+ScratchRecord g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+moe_status scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ScratchRecord& r = g_scratch[dev];
+  if (!r.ready) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return MOE_ERR_HIP;
+    r.ptr = ptr;
+    r.ready = true;
+  }
+  *out = r.ptr;
+  return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" {
+
+moe_status moe_experts_forward(const moe_problem* p, const void* hidden, const int32_t* topk_idx, const float* topk_w,
+                               const void* w_gate_up, const void* w_down, const void* w_gate_up_scale,
+                               const void* w_down_scale, void* out, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  moe_status st = check_forward_args(p, hidden, topk_idx, topk_w, w_gate_up, w_down, w_gate_up_scale, w_down_scale,
+                                     out);
+  if (st != MOE_OK || p->T == 0) return st;
+  if (!workspace) return MOE_ERR_NULL_ARG;
+  if (!aligned16(workspace)) return MOE_ERR_BAD_SHAPE;
+  if (workspace_bytes < make_layout(*p).total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  DeviceRecord* dev = nullptr;
+  if ((st = device_record(&dev)) != MOE_OK) return st;
+  return forward_launch(p, hidden, topk_idx, topk_w, w_gate_up, w_down, w_gate_up_scale, w_down_scale, out, workspace,
+                        dev, stream);
+}
+
+size_t moe_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+moe_status moe_experts_forward_noalloc(const moe_problem* p, const void* hidden, const int32_t* topk_idx,
+                                       const float* topk_w, const void* w_gate_up, const void* w_down,
+                                       const void* w_gate_up_scale, const void* w_down_scale, void* out,
+                                       void* stream) {
+  moe_status st = check_forward_args(p, hidden, topk_idx, topk_w, w_gate_up, w_down, w_gate_up_scale, w_down_scale,
+                                     out);
+  if (st != MOE_OK || p->T == 0) return st;
+  if (make_layout(*p).total > kNoAllocScratchBytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  DeviceRecord* dev = nullptr;
+  if ((st = device_record(&dev)) != MOE_OK) return st;
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws)) != MOE_OK) return st;
+  return forward_launch(p, hidden, topk_idx, topk_w, w_gate_up, w_down, w_gate_up_scale, w_down_scale, out, ws, dev,
+                        stream);
 }
 
 moe_status moe_set_stage_events(void* const* events, int n) {

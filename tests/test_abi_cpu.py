@@ -265,3 +265,25 @@ def test_check_scales_rejects(case):
     }[case]
     with pytest.raises(ValueError):
         m.check_scales(*args)
+
+
+# ----------------------------------------------------------------------------- allocation-free forward
+
+def test_noalloc_rejects_problems_beyond_its_array_before_any_hip_call():
+    L = m.lib()
+    cap = L.moe_noalloc_scratch_bytes()
+    assert cap == 128 << 20
+    fake = ctypes.c_void_p(1 << 20)     # aligned stand-ins: the size check comes before any HIP call
+    big = P(act=m.BF16, weight=m.BF16, T=8192, H=7168, I=2048, E=256, k=8)
+    assert m.workspace_size(big) > cap
+    st = L.moe_experts_forward_noalloc(ctypes.byref(big), fake, fake, fake, fake, fake, None, None, fake, None)
+    assert st == m.ERR_WORKSPACE
+    # the Qwen-shaped prefill layer fits
+    qwen = P(act=m.BF16, weight=m.BF16, T=4096, H=2048, I=1408, E=60, k=4)
+    assert m.workspace_size(qwen) <= cap
+    # argument errors as for the forward
+    assert L.moe_experts_forward_noalloc(None, fake, fake, fake, fake, fake, None, None, fake, None) == m.ERR_NULL_ARG
+    assert L.moe_experts_forward_noalloc(ctypes.byref(qwen), None, fake, fake, fake, fake, None, None, fake,
+                                         None) == m.ERR_NULL_ARG
+    t0 = P(act=m.BF16, weight=m.BF16, T=0)
+    assert L.moe_experts_forward_noalloc(ctypes.byref(t0), None, None, None, None, None, None, None, None, None) == m.OK
