@@ -40,7 +40,6 @@ def test_traffic_record_matches_current_sources(fname):
 
 
 def test_default_workload_is_the_largest_single_gpu_layer():
-    import argparse
     assert bench.WORKLOADS["dsv3_prefill_bf16"].startswith("DeepSeek-V3-shaped bf16 prefill")
     spec = synth.spec_for("dsv3_prefill_bf16")
     flops, byts = bench.algorithmic(spec, 187, "gate_up")
