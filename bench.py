@@ -8,9 +8,10 @@ quantisation,) gate/up GEMM + SwiGLU, down GEMM + weighted combine, finalize --
 over one batch of seeded synthetic inputs already resident in HBM.  The default
 workload is the DeepSeek-V3-shaped bf16 prefill layer (T=8192, H=7168, I=2048,
 E=256, top-8, Zipf-skewed routing), the largest layer of the set that fits one GPU.
-Each timed forward is bracketed by HIP events on the library's stream, and 1 GiB of
-scratch is written between forwards (outside the events) so that no step starts with
-the previous step's data in the 256 MB Infinity Cache.  Prints one JSON line:
+Each timed forward is bracketed by HIP events on the library's stream.  Between forwards
+(outside the events) 1 GiB of scratch is written and a second 1 GiB buffer is read, so
+that every step starts with the 4 MB L2s and the 256 MB Infinity Cache cold and clean
+(a write alone would leave dirty lines for the step to write back).  Prints one JSON line:
 tokens/s from the median step, the step's median/min/max, the dominant kernel's
 roofline figures (its launches bracketed by HIP events in every timed step), and
 the CPU oracle timed on bounded samples (expert-major fp64 BLAS over all host
@@ -328,9 +329,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=30.0)
     ap.add_argument("--flush-mib", type=int, default=1024,
                     help="MiB of scratch touched between timed steps (outside the step events)")
-    ap.add_argument("--flush", choices=("write", "read", "none"), default="write",
-                    help="how the scratch evicts the caches: written (leaves dirty lines the next "
-                         "step writes back), read (clean lines), or not at all")
+    ap.add_argument("--flush", choices=("write+read", "write", "read", "none"), default="write+read",
+                    help="how scratch evicts the caches between steps: written and then a second buffer "
+                         "read (the caches are cold and clean when the step starts), written only (dirty "
+                         "lines the step has to write back), read only, or not at all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 256 MiB device copy (counter calibration for the traffic figure)")
@@ -397,6 +399,7 @@ def main():
     # timed region: every forward bracketed by step events, the dominant kernel by stage
     # events; a scratch write between forwards (outside the step events) evicts the cache
     flush = torch.zeros(max(args.flush_mib, 1) << 20, dtype=torch.uint8, device=dev)
+    flush_r = torch.zeros_like(flush) if args.flush == "write+read" else flush
     tev = hev.create(2 * args.steps)
     sev = hev.create(2 * args.steps)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
@@ -406,10 +409,10 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        if args.flush == "write":
+        if args.flush in ("write", "write+read"):
             flush.fill_(i & 0xFF)
-        elif args.flush == "read":
-            torch.amax(flush)
+        if args.flush in ("read", "write+read"):
+            torch.amax(flush_r)
         handles[2 * dom], handles[2 * dom + 1] = tev[2 * i], tev[2 * i + 1]
         m.set_stage_events(handles)
         rec(ctypes.c_void_p(sev[2 * i]), stream)
@@ -422,7 +425,7 @@ def main():
     step_ms = [hev.elapsed_ms(sev[2 * i], sev[2 * i + 1]) for i in range(args.steps)]
     hev.destroy(tev)
     hev.destroy(sev)
-    del flush
+    del flush, flush_r
 
     step_st, kern_st = _stats(step_ms), _stats(kern_ms)
     ms_per_step = step_st["median"]

@@ -437,6 +437,11 @@ moe_status forward_launch(const moe_problem* p, const void* hidden, const int32_
   g.gate = (p->flags & MOE_FLAG_ACT_GELU) ? kGateGelu : ((p->flags & MOE_FLAG_ACT_RELU) ? kGateRelu : kGateSilu);
   g.offsets = offsets;
   g.mt = mt;
+  // grouped GEMM items in blocks of 8 M tiles x 4 N tiles (the 32 workgroups of an XCD in
+  // one round): measured on the DeepSeek-shaped bf16 layer, the same time as M-fastest order
+  // (7.57-7.62 ms per step for blocks of 0, 4, 8 and 16 M tiles) with fewer operand fetches
+  // beyond L2
+  g.item_mb = 8;
   g.I = p->I;
   g.H = p->H;
   g.k = p->k;

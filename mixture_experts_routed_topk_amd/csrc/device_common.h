@@ -143,6 +143,30 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
+// Work item `local` of one expert's mt_e x NT tiles -> (N tile nt, M tile m).  The items go
+// in blocks of mb M tiles x nb N tiles (nb = 32 / mb, the workgroups of one XCD in one
+// round), M fastest inside a block, the blocks of a group of mb M tiles in N order, the
+// groups in M order; the last group and block may be smaller.  The tiles that run together
+// on one XCD then share mb row tiles and nb weight tiles in its L2 instead of one weight
+// tile and 32 row tiles.  mb <= 0: M fastest over the whole expert (nt = local / mt_e).
+__device__ __forceinline__ void blocked_tile(int local, int mt_e, int NT, int mb, int& nt, int& m) {
+  if (mb <= 0) {
+    nt = local / mt_e;
+    m = local - nt * mt_e;
+    return;
+  }
+  const int nb = mb >= 32 ? 1 : 32 / mb;
+  const int full = mt_e / mb;                  // groups of exactly mb M tiles
+  int mg = local / (mb * NT);
+  const int msz = mg < full ? mb : mt_e - full * mb;
+  if (mg > full) mg = full;
+  const int l2 = local - mg * mb * NT;         // index inside the group, [0, msz * NT)
+  const int nbk = l2 / (msz * nb);             // block of nb N tiles (the last may be short)
+  const int l3 = l2 - nbk * msz * nb;
+  nt = nbk * nb + l3 / msz;
+  m = mg * mb + l3 % msz;
+}
+
 // Largest e in [0, E) with start[e] * nt <= w (start is non-decreasing, start[E] * nt > w).
 __device__ __forceinline__ int find_group(const int32_t* __restrict__ start, int E, int nt, int w) {
   int lo = 0, hi = E - 1;

@@ -133,8 +133,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_bf16_kernel(GroupedArgs g
     const int mt0 = mt_at(e);
     const int mt_e = mt_at(e + 1) - mt0;
     const int local = w - mt0 * g.NT;
-    const int nt = local / mt_e;
-    const int mloc = local - nt * mt_e;
+    int nt, mloc;
+    blocked_tile(local, mt_e, g.NT, g.item_mb, nt, mloc);
     const int off0 = g.offsets[e], off1 = g.offsets[e + 1];
     const int cnt = off1 - off0;
     const int per = min(BM, ((cnt + mt_e - 1) / mt_e + 31) & ~31);

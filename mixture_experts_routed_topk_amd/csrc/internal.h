@@ -60,6 +60,7 @@ struct GroupedArgs {
   int NT;                   // number of N tiles
   const int32_t* offsets;   // [E+1] sorted-row offsets per expert
   const int32_t* mt;        // [E+1] M-tile starts for this GEMM's tile height
+  int item_mb;              // work-item order: blocks of item_mb M tiles (blocked_tile)
   // gate_up epilogue
   int I;                    // intermediate size (up rows start at I)
   void* act_out;            // [A][I] SwiGLU output: bf16 / f32, or e4m3 codes (fp8, fp4)
