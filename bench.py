@@ -184,15 +184,24 @@ KERNEL_SOURCES = {   # (path, weight dtype, stage) -> kernel source files, for t
 }
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and blank lines (a comment edit does not change a kernel)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]
+    return "\n".join(ln for ln in lines if ln.strip())
+
+
 def kernel_digest(path: str, weight: str, stage: str) -> tuple[str, str]:
-    """(name, sha256) of the dominant kernel's sources (its file + the shared device headers)."""
+    """(name, sha256) of the dominant kernel's code (its file + the shared device headers,
+    comments left out)."""
     import hashlib
     files = KERNEL_SOURCES[(path, weight, stage)]
     csrc = os.path.join(ROOT, "mixture_experts_routed_topk_amd", "csrc")
     h = hashlib.sha256()
-    for f in files + ["device_common.h", "internal.h"]:
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
+    for f in files + ["device_common.h", "internal.h"] + (["act_quant_epilogue.h"] if weight in ("fp8", "fp4") else []):
+        with open(os.path.join(csrc, f)) as fh:
+            h.update(_code_only(fh.read()).encode())
     return files[0].rsplit(".", 1)[0], h.hexdigest()
 
 
@@ -310,6 +319,41 @@ def cpu_baseline(spec, D, seconds: float):
             "literal": {"value": n_lit / t_lit, "unit": "tokens/s", "cores": 1,
                         "sample": f"first {n_lit} tokens, per-token fp64 loop over the k chosen experts, "
                                   f"{t_lit:.1f} s"}}
+
+
+def machine_peaks(dev, reps: int = 5):
+    """What this machine delivers, as context for the published peaks: HBM read bandwidth (a float32
+    sum over 2 GiB), copy bandwidth (2 GiB read + 2 GiB written) and a dense 8192^3 bf16 GEMM
+    (torch.matmul, hipBLASLt); each the median of `reps` runs timed with events.  None of them
+    is part of the experts forward."""
+    import torch
+    n = 2 << 30
+    x = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    a = torch.randn((8192, 8192), dtype=torch.bfloat16, device=dev)
+    b = torch.randn((8192, 8192), dtype=torch.bfloat16, device=dev)
+
+    def timed(fn):
+        fn()
+        out = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            out.append(e0.elapsed_time(e1))
+        return sorted(out)[len(out) // 2]
+
+    ms_sum = timed(lambda: torch.sum(x))
+    ms_copy = timed(lambda: y.copy_(x))
+    ms_mm = timed(lambda: torch.matmul(a, b))
+    del x, y, a, b
+    gbs = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9   # noqa: E731
+    return {"hbm_read_GBs": gbs(n, ms_sum), "hbm_copy_GBs": gbs(2 * n, ms_copy),
+            "bf16_gemm_TFLOPs": 2.0 * 8192 ** 3 / (ms_mm * 1e-3) / 1e12,
+            "how": "median of 5: torch.sum over 2 GiB float32 (read), 2 GiB device copy (read + write), "
+                   "torch.matmul 8192^3 bf16 (hipBLASLt)"}
 
 
 def _stats(v):
@@ -477,6 +521,12 @@ def main():
         "roofline": roof,
     }
     res["router_step"] = router_step(spec, dev)
+    mp = machine_peaks(dev)
+    # context only: torch's read and copy kernels stream below what the decode kernels reach, so
+    # the measured-peak fraction is given against the dense bf16 GEMM only
+    meas = mp["bf16_gemm_TFLOPs"] if roof["bound"] == "mfma" and spec.weight == "bf16" else None
+    res["machine"] = mp
+    roof["frac_of_measured"] = roof["achieved"] / meas if meas else None
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(spec, D, args.cpu_seconds)
     print(json.dumps(res), flush=True)

@@ -32,10 +32,11 @@
 // distinct banks.  A rows past the tile's last 32-row fragment are neither loaded nor
 // multiplied.
 //
-// Work items are (expert, N tile, M tile) with M fastest; an expert's rows are split
-// evenly over its M tiles (multiples of 32 rows, at most 160).  The grid is persistent
-// and each round hands every XCD (blockIdx % 8) a contiguous run of items, so the M tiles
-// sharing a weight tile run at the same pace on one XCD and meet in its L2.  The M-tile
+// Work items are (expert, N tile, M tile), an expert's items in blocks of 8 M tiles x 4 N
+// tiles (blocked_tile); an expert's rows are split evenly over its M tiles (multiples of 32
+// rows, at most 160).  The grid is persistent and each round hands every XCD (blockIdx % 8)
+// a contiguous run of items, so the tiles of a block run at the same pace on one XCD and
+// share their row and weight tiles in its L2.  The M-tile
 // table lives in LDS as 16-bit entries (read from global memory when it does not fit).
 #include <type_traits>
 

@@ -24,8 +24,9 @@
 // LDS ring through global->LDS DMA; slices kt + 1 and kt + 2 stream in while slice kt is
 // multiplied.  Rows are stored with their 16-byte chunks XOR-permuted (A: by (row >> 1) & 7
 // over 8 chunks, B: by (row >> 2) & 3 over 4 chunks) so the fragment reads are free of bank
-// conflicts.  Work items (expert, N tile, M tile), M fastest, an expert's rows split evenly
-// over its M tiles (multiples of 32 rows); persistent grid with XCD-contiguous runs of items.
+// conflicts.  Work items (expert, N tile, M tile) in blocks of 8 M tiles x 4 N tiles
+// (blocked_tile), an expert's rows split evenly over its M tiles (multiples of 32 rows);
+// persistent grid with XCD-contiguous runs of items.
 #include <type_traits>
 
 #include "act_quant_epilogue.h"

@@ -26,8 +26,9 @@
 // and kt + 2 stream in while slice kt is multiplied, the DMA of kt + 2 spread over the
 // slice's work.  Slot rows are 128 bytes with 16-byte chunks XOR-permuted by
 // (row >> 1) & 7; the row scales of the slice ride in the slot.  Work items (expert,
-// N tile, M tile), M fastest, an expert's rows split evenly over its M tiles (multiples
-// of 32 rows, at most 128); persistent grid with XCD-contiguous runs of items.
+// N tile, M tile) in blocks of 8 M tiles x 4 N tiles (blocked_tile), an expert's rows split
+// evenly over its M tiles (multiples of 32 rows, at most 128); persistent grid with
+// XCD-contiguous runs of items.
 #include <type_traits>
 
 #include "act_quant_epilogue.h"
