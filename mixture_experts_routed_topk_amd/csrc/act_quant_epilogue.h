@@ -8,11 +8,12 @@
 // element becomes e4m3(a / s) (float32 division, round to nearest even, saturating).  A
 // gate_up tile holds exactly one such group per row (128 SwiGLU columns, I % 128 == 0), so
 // the group never leaves the workgroup: each wave reduces its 32 columns of a row across
-// its 16 lanes, the four column waves meet in LDS, and the codes are staged in LDS and
-// written as 16-byte pieces of the [rows][I] code matrix, with one float32 scale per row
-// and tile in the [rows][I / 128] scale matrix.  The values quantised are the same float32
-// values a separate pass would read back, so the codes and scales are those of the row
-// quantiser applied to them.
+// its 16 lanes and the four column waves meet in LDS; then each lane stores its codes
+// straight from registers (the 16 lanes of a group write 16 consecutive bytes of a row of
+// the [rows][I] code matrix; staging them in LDS for 16-byte stores measured 1-3% slower),
+// with one float32 scale per row and tile in the [rows][I / 128] scale matrix.  The values
+// quantised are the same float32 values a separate pass would read back, so the codes and
+// scales are those of the row quantiser applied to them.
 //
 // Tile layout (shared by both kernels): 128 rows; wave (wm, wn) of the 2 x 4 grid holds,
 // for row fragment i, rows (2 i + wm) * 16 + 4 g4 + q (q < 4, g4 = lane >> 4) and, in
@@ -26,20 +27,19 @@ namespace moe {
 
 constexpr int kActQRows = 128;          // tile rows
 constexpr int kActQCols = 128;          // SwiGLU columns per tile (one scale group)
-// LDS bytes the epilogue needs: the staged codes and the per-wave row maxima
-constexpr int kActQLdsBytes = kActQRows * kActQCols + kActQRows * 4 * 4;
+// LDS bytes the epilogue needs: the per-wave row maxima
+constexpr int kActQLdsBytes = kActQRows * 4 * 4;
 
-// Every wave of the 512-thread workgroup must call this (it holds two barriers), after a
+// Every wave of the 512-thread workgroup must call this (it holds a barrier), after a
 // barrier that ends all reads of `lds`.  rows: valid tile rows; row0: the tile's first row
 // in the code matrix; nt: the tile's column group; I: columns of the code matrix.
 template <int MFRAG>
 __device__ __forceinline__ void gateup_requant_epilogue(const f32x4 (&acc)[MFRAG][4], int gate, int wm, int wn,
-                                                        int l16, int g4, int tid, int rows, int row0, int nt, int I,
+                                                        int l16, int g4, int rows, int row0, int nt, int I,
                                                         char* lds, uint8_t* __restrict__ codes,
                                                         float* __restrict__ scales) {
   static_assert(2 * 16 * MFRAG == kActQRows, "two row waves of MFRAG 16-row fragments");
-  uint8_t* sQ = reinterpret_cast<uint8_t*>(lds);
-  float* sAmax = reinterpret_cast<float*>(lds + kActQRows * kActQCols);   // [row][wn]
+  float* sAmax = reinterpret_cast<float*>(lds);   // [row][wn]
   float v[MFRAG][4][2];
 #pragma unroll
   for (int i = 0; i < MFRAG; ++i)
@@ -67,16 +67,13 @@ __device__ __forceinline__ void gateup_requant_epilogue(const f32x4 (&acc)[MFRAG
       const f32x4 mm = *reinterpret_cast<const f32x4*>(&sAmax[r * 4]);
       const float amax = fmaxf(fmaxf(mm[0], mm[1]), fmaxf(mm[2], mm[3]));
       const float s = amax > 0.f ? amax / 448.0f : 1.0f;   // correctly rounded division
+      if (r < rows) {
+        uint8_t* o = codes + (int64_t)(row0 + r) * I + nt * kActQCols + 32 * wn + l16;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) sQ[r * kActQCols + 32 * wn + 16 * j + l16] = (uint8_t)f32_to_e4m3(v[i][q][j] / s);
-      if (wn == 0 && l16 == 0 && r < rows) scales[(int64_t)(row0 + r) * gpr + nt] = s;
+        for (int j = 0; j < 2; ++j) o[16 * j] = (uint8_t)f32_to_e4m3(v[i][q][j] / s);
+        if (wn == 0 && l16 == 0) scales[(int64_t)(row0 + r) * gpr + nt] = s;
+      }
     }
-  __syncthreads();
-  for (int c = tid; c < rows * (kActQCols / 16); c += 512) {
-    const int r = c >> 3, part = c & 7;
-    const i32x4 val = *reinterpret_cast<const i32x4*>(sQ + r * kActQCols + 16 * part);
-    *reinterpret_cast<i32x4*>(codes + (int64_t)(row0 + r) * I + nt * kActQCols + 16 * part) = val;
-  }
 }
 
 }  // namespace moe

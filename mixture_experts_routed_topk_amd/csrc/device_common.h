@@ -149,7 +149,7 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 // groups in M order; the last group and block may be smaller.  The tiles that run together
 // on one XCD then share mb row tiles and nb weight tiles in its L2 instead of one weight
 // tile and 32 row tiles.  mb <= 0: M fastest over the whole expert (nt = local / mt_e).
-__device__ __forceinline__ void blocked_tile(int local, int mt_e, int NT, int mb, int& nt, int& m) {
+__host__ __device__ __forceinline__ void blocked_tile(int local, int mt_e, int NT, int mb, int& nt, int& m) {
   if (mb <= 0) {
     nt = local / mt_e;
     m = local - nt * mt_e;

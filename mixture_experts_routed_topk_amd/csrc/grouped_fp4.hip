@@ -269,7 +269,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_fp4_kernel(GroupedArgs g)
     // bcol0(j) + l16
     if constexpr (MODE == kGateUp) {
       __syncthreads();   // every wave is done with the ring
-      gateup_requant_epilogue<MFRAG>(acc, g.gate, wm, wn, l16, g4, tid, rows, row0, nt, g.I, &ring[0][0],
+      gateup_requant_epilogue<MFRAG>(acc, g.gate, wm, wn, l16, g4, rows, row0, nt, g.I, &ring[0][0],
                                      static_cast<uint8_t*>(g.act_out), g.act_scale_out);
     } else {
       if (tid < BM) {
