@@ -233,6 +233,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_bf16_kernel(GroupedArgs g
       if constexpr (NI > 0) load_frags(0, 0);
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
+        if (next) issue_part(kt2, nslot, s);
         if constexpr (NI > 0) {
           if (s + 1 < KSTEPS) load_frags(s + 1, (s + 1) & 1);
 #pragma unroll
@@ -241,7 +242,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_bf16_kernel(GroupedArgs g
             for (int j = 0; j < NFRAG; ++j) acc[i][j] = mfma_32x32x16_bf16(fa[s & 1][i], fb[s & 1][j], acc[i][j]);
           }
         }
-        if (next) issue_part(kt2, nslot, s);
       }
     };
     // three-slot ring: slices kt + 1 and kt + 2 stream in while slice kt is multiplied
