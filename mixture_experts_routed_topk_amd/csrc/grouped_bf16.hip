@@ -13,7 +13,9 @@
 //   down    : rows = the SwiGLU rows (already in sorted order), weights W_down[e]
 //             ([H, I], K = I contiguous).  The epilogue scales each row by its routing
 //             weight and adds it into the token's float32 output row (hardware float
-//             atomics), or stores it to the slot's own row for the deterministic combine.
+//             atomics), or stores it to the slot's own row: float32 for the deterministic
+//             combine, or bf16 rows staged through LDS and written in 16-byte pieces (the
+//             default combine of bf16 layers).
 //
 // A workgroup of eight waves (two per SIMD, so one wave's LDS and barrier waits are
 // covered by the other's MFMAs) computes a tile of up to 160 rows x 256 columns with
@@ -291,6 +293,36 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_bf16_kernel(GroupedArgs g
         if (col < ncols)
           *reinterpret_cast<i32x4*>(out + (int64_t)(row0 + r) * g.I + col) =
               *reinterpret_cast<const i32x4*>(stage + r * 128 + piece * 8);
+      }
+    } else if constexpr (MODE == kDownSlotsBf16) {
+      // weighted rows as bf16, staged through LDS as [BM rows][256 columns] and written to
+      // the slots' rows in 16-byte pieces
+      if (tid < BM) {
+        sTok[tid] = my_tok;
+        sWt[tid] = my_wt;
+      }
+      __syncthreads();
+      uint16_t* stage = reinterpret_cast<uint16_t*>(&ring[0][0]);
+#pragma unroll
+      for (int i = 0; i < MFRAG; ++i) {
+        if ((2 * i + wm) * 32 >= rows) break;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = (2 * i + wm) * 32 + 8 * (v >> 2) + 4 * hgrp + (v & 3);
+          const float wt = sWt[r];
+#pragma unroll
+          for (int j = 0; j < NFRAG; ++j)
+            stage[r * BN + tile_col0(j) + r32] = (uint16_t)f32_to_bf16_bits(wt * acc[i][j][v]);
+        }
+      }
+      __syncthreads();
+      uint16_t* out = reinterpret_cast<uint16_t*>(g.slot_out);
+      for (int c = tid; c < rows * (BN / 8); c += kThreads) {
+        const int r = c / (BN / 8), piece = c % (BN / 8);
+        const int col = nt * BN + piece * 8;
+        if (col < ncols)
+          *reinterpret_cast<i32x4*>(out + (int64_t)sTok[r] * g.H + col) =
+              *reinterpret_cast<const i32x4*>(stage + r * BN + piece * 8);
       }
     } else {
       if (tid < BM) {
