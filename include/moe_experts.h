@@ -129,12 +129,12 @@ const char* moe_status_str(moe_status s);
  * and their activations, never a copy of a weight.  Grows with T*k*(I + H) and T*H.
  * Errors: NULL_ARG (p or bytes NULL), BAD_SHAPE / UNSUPPORTED as for the forward.  When the k rows of a
  * token are combined as per-slot rows (always with MOE_FLAG_DETERMINISTIC; by default
- * while 4*T*k*H <= 512 MiB, or 2*T*k*H <= 1 GiB for a bf16 layer, where that combine is
+ * while 4*T*k*H <= 512 MiB, or 2*T*k*H <= 1 GiB for a bf16, fp8 or fp4 layer, where that combine is
  * the faster one; never with MOE_FLAG_ATOMIC_COMBINE) it holds a [T*k, H] buffer instead
  * of the float32 [T, H]
  * accumulator: float32 rows with MOE_FLAG_DETERMINISTIC, and bf16 rows (each slot's
- * weighted row rounded once, the k rows summed in float32) on the default bf16
- * grouped path. */
+ * weighted row rounded once, the k rows summed in float32) on the default grouped path
+ * of bf16, fp8 and fp4 layers. */
 moe_status moe_workspace_size(const moe_problem* p, size_t* bytes);
 
 /*

@@ -16,7 +16,8 @@
 // for the down projection (act_quant_epilogue.h).  down: 256 output
 // columns; the epilogue multiplies by the routing weight and adds the row into the token's
 // float32 output row (hardware float atomics) or stores it to the slot's own row
-// (per-slot combine).
+// (per-slot combine: float32 rows, or by default bf16 rows staged through LDS and written
+// in 16-byte pieces).
 //
 // Tiles of up to 128 rows x 256 weight rows; eight waves in a 2 x 4 grid, wave (wm, wn)
 // owning the 16-row fragments wm, wm + 2, .., wm + 6 and four 16-column fragments (down:
@@ -57,7 +58,7 @@ constexpr int kMaxKB = 512;                // K / 128 (K = I <= 65536)
 static_assert(ALD <= 4 && BLD == 4, "the DMA of a slice is spread over four parts");
 static_assert(BM == kActQRows && BN / 2 == kActQCols && NSTAGE * STAGE >= kActQLdsBytes, "epilogue tile");
 
-enum { kGateUp = 0, kDownAtomic = 1, kDownSlots = 2 };
+enum { kGateUp = 0, kDownAtomic = 1, kDownSlots = 2, kDownSlotsBf16 = 3 };
 
 __device__ __forceinline__ int chunk_slot(int row, int c) { return c ^ ((row >> 1) & 7); }
 
@@ -291,6 +292,36 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_fp8_kernel(GroupedArgs g)
       __syncthreads();   // every wave is done with the ring
       gateup_requant_epilogue<MFRAG>(acc, g.gate, wm, wn, l16, g4, rows, row0, nt, g.I, &ring[0][0],
                                      static_cast<uint8_t*>(g.act_out), g.act_scale_out);
+    } else if constexpr (MODE == kDownSlotsBf16) {
+      // weighted rows as bf16, staged through LDS as [BM rows][BN columns] and written to the
+      // slots' rows in 16-byte pieces
+      if (tid < BM) {
+        sTok[tid] = my_tok;
+        sWt[tid] = my_wt;
+      }
+      __syncthreads();
+      uint16_t* stage = reinterpret_cast<uint16_t*>(&ring[0][0]);
+#pragma unroll
+      for (int i = 0; i < MFRAG; ++i) {
+        if ((2 * i + wm) * 16 >= rows) break;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = (2 * i + wm) * 16 + 4 * g4 + q;
+          const float wt = sWt[r];
+#pragma unroll
+          for (int j = 0; j < NFRAG; ++j)
+            stage[r * BN + bcol0(j) + l16] = (uint16_t)f32_to_bf16_bits(wt * acc[i][j][q]);
+        }
+      }
+      __syncthreads();
+      uint16_t* out = reinterpret_cast<uint16_t*>(g.slot_out);
+      for (int c = tid; c < rows * (BN / 8); c += kThreads) {
+        const int r = c / (BN / 8), piece = c % (BN / 8);
+        const int col = nt * BN + piece * 8;
+        if (col < ncols)
+          *reinterpret_cast<i32x4*>(out + (int64_t)sTok[r] * g.H + col) =
+              *reinterpret_cast<const i32x4*>(stage + r * BN + piece * 8);
+      }
     } else {
       if (tid < BM) {
         sTok[tid] = my_tok;
@@ -337,7 +368,8 @@ int down_fp8_cols() { return BN; }
 hipError_t launch_gateup_fp8(const GroupedArgs& g, int grid, hipStream_t s) { return launch<kGateUp>(g, grid, s); }
 
 hipError_t launch_down_fp8(const GroupedArgs& g, int grid, hipStream_t s) {
-  return g.slot_out ? launch<kDownSlots>(g, grid, s) : launch<kDownAtomic>(g, grid, s);
+  if (!g.slot_out) return launch<kDownAtomic>(g, grid, s);
+  return g.slot_bf16 ? launch<kDownSlotsBf16>(g, grid, s) : launch<kDownSlots>(g, grid, s);
 }
 
 }  // namespace moe

@@ -102,11 +102,18 @@ def test_workspace_by_combine():
     assert nb_default - nb_atomic == 2 * Ab * Hb - 4 * Tb * Hb
     assert "combine=slot_rows_bf16" in m.plan_describe(P(act=m.BF16, weight=m.BF16, T=8192, H=7168, I=2048,
                                                          E=256, k=8))
+    # ... as do fp8 and fp4 layers (their down kernels share the bf16 slot-row epilogue) ...
+    fp8 = P(act=m.BF16, weight=m.FP8_E4M3, scale=m.SCALE_F32, T=4096, H=7168, I=2048, E=256, k=8)
+    assert "combine=slot_rows_bf16" in m.plan_describe(fp8)
+    fp4 = P(act=m.BF16, weight=m.FP4_E2M1, scale=m.SCALE_UE8M0, T=4096, H=7168, I=2048, E=256, k=8)
+    assert "combine=slot_rows_bf16" in m.plan_describe(fp4)
     # ... and above that, or for float32 rows above 512 MiB, the default is the atomic combine
     bigger = P(act=m.BF16, weight=m.BF16, T=9363, H=7168, I=2048, E=256, k=8)   # 2*T*k*H > 1 GiB
     assert "combine=atomic_f32" in m.plan_describe(bigger)
-    fp8 = P(act=m.BF16, weight=m.FP8_E4M3, scale=m.SCALE_F32, T=4096, H=7168, I=2048, E=256, k=8)
+    fp8.T = 9363
     assert "combine=atomic_f32" in m.plan_describe(fp8)
+    f32 = P(act=m.F32, weight=m.F32, T=2341, H=7168, I=2048, E=256, k=8)        # 4*T*k*H > 512 MiB
+    assert "combine=atomic_f32" in m.plan_describe(f32)
     p.flags = m.FLAG_DETERMINISTIC | m.FLAG_ATOMIC_COMBINE
     assert _ws(p)[0] == m.ERR_UNSUPPORTED
 
