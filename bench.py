@@ -127,12 +127,17 @@ def router_step(spec, dev, iters=50):
 
 
 def algorithmic(spec, active_count, stage):
-    """(flops, bytes) the method must do/move in one launch of a stage."""
+    """(flops, bytes) the method must do/move in one launch of a stage.
+
+    Bytes are the active experts' weights and weight scales, the layer's input rows (gate_up:
+    x, or its e4m3 codes and row scales on fp8 and fp4 layers) and its output rows (down:
+    out).  The SwiGLU rows `a` that pass from gate_up to down, and the combine's accumulator or
+    slot rows, belong to this two-kernel design rather than to the method: they are counted
+    apart (`intermediate_bytes`), not here."""
     A, H, I = spec.A, spec.H, spec.I
     wb = {"f32": 4, "bf16": 2, "fp8": 1, "fp4": 0.5}[spec.weight]
     xb = {"f32": 4, "bf16": 2}[spec.act]
-    ab = {"f32": 4, "bf16": 2, "fp8": 1, "fp4": 1}[spec.weight]   # SwiGLU rows as stored
-    q = spec.weight in ("fp8", "fp4")                               # e4m3 activation rows
+    q = spec.weight in ("fp8", "fp4")                               # e4m3 input rows
     # weight-scale bytes per weight element: 128x128 blocks (fp8) or 1x32 UE8M0 (fp4)
     sb = 0.0
     if spec.weight == "fp8":
@@ -142,18 +147,24 @@ def algorithmic(spec, active_count, stage):
     if stage == "gate_up":
         flops = 4.0 * A * H * I
         byts = active_count * 2 * I * H * (wb + sb)
-        byts += spec.T * H * (1 if q else xb) + A * I * ab
+        byts += spec.T * H * (1 if q else xb)
         if q:
-            byts += spec.T * (H // 128) * 4 + A * (I // 128) * 4
+            byts += spec.T * (H // 128) * 4
     elif stage == "down":
         flops = 2.0 * A * H * I
-        byts = active_count * H * I * (wb + sb)
-        byts += A * I * ab + spec.T * H * 4
-        if q:
-            byts += A * (I // 128) * 4
+        byts = active_count * H * I * (wb + sb) + spec.T * H * xb
     else:
         raise ValueError(stage)
     return flops, float(byts)
+
+
+def intermediate_bytes(spec, stage):
+    """Bytes of the SwiGLU rows `a` one launch of a stage writes (gate_up) or reads (down):
+    bf16 or float32 rows, or e4m3 codes with one float32 scale per 128 columns."""
+    A, I = spec.A, spec.I
+    if spec.weight in ("fp8", "fp4"):
+        return float(A * I + A * (I // 128) * 4)
+    return float(A * I * {"f32": 4, "bf16": 2}[spec.weight])
 
 
 def layer_totals(spec, active_count):
@@ -490,6 +501,7 @@ def main():
                  "median_ms": kern_st["median"], "min_ms": kern_st["min"], "max_ms": kern_st["max"],
                  "launches": len(kern_ms),
                  "algorithmic_flops": flops, "algorithmic_bytes": byts,
+                 "intermediate_bytes": intermediate_bytes(spec, dominant),
                  "mfma_frac": flops / (kavg * 1e-3) / 1e12 / peak_f,
                  "hbm_frac": byts / (kavg * 1e-3) / 1e9 / PEAK_HBM_GBS})
     lf, lb = layer_totals(spec, n_active)

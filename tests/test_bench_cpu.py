@@ -44,14 +44,26 @@ def test_default_workload_is_the_largest_single_gpu_layer():
     spec = synth.spec_for("dsv3_prefill_bf16")
     flops, byts = bench.algorithmic(spec, 187, "gate_up")
     assert flops == 4.0 * 65536 * 7168 * 2048                      # 3.85 TFLOP
-    assert byts == 187 * 2 * 2048 * 7168 * 2 + 8192 * 7168 * 2 + 65536 * 2048 * 2
+    assert byts == 187 * 2 * 2048 * 7168 * 2 + 8192 * 7168 * 2       # weights + x; not `a`
+    assert bench.intermediate_bytes(spec, "gate_up") == 65536 * 2048 * 2
+
+
+def test_fp8_algorithmic_counts():
+    spec = synth.spec_for("dsv3_fp8_f32scale")
+    _, byts = bench.algorithmic(spec, 157, "gate_up")
+    # e4m3 weights + one float32 scale per 128x128 block, x codes + their row scales
+    assert byts == 157 * 2 * 2048 * 7168 * (1 + 4 / 16384) + 4096 * 7168 + 4096 * 56 * 4
+    assert bench.intermediate_bytes(spec, "down") == 32768 * 2048 + 32768 * 16 * 4
 
 
 def test_qwen_prefill_algorithmic_counts():
     spec = synth.spec_for("qwen_prefill_bf16")
     flops, byts = bench.algorithmic(spec, 60, "gate_up")
     assert flops == 4.0 * 16384 * 2048 * 1408                      # 189.0 GFLOP
-    assert byts == 60 * 2 * 1408 * 2048 * 2 + 4096 * 2048 * 2 + 16384 * 1408 * 2   # 755.0 MB
+    assert byts == 60 * 2 * 1408 * 2048 * 2 + 4096 * 2048 * 2      # 709.0 MB
+    df, db = bench.algorithmic(spec, 60, "down")
+    assert df == 2.0 * 16384 * 2048 * 1408
+    assert db == 60 * 1408 * 2048 * 2 + 4096 * 2048 * 2             # W_down + out
     lf, lb = bench.layer_totals(spec, 60)
     assert lf == 6.0 * 16384 * 2048 * 1408
     assert lb == 60 * 3 * 1408 * 2048 * 2 + 2 * 4096 * 2048 * 2 + 8 * 16384
