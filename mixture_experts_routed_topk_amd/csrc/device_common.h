@@ -20,16 +20,16 @@ __device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float
 __device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// float -> bf16 bits, round to nearest even; NaN -> canonical quiet NaN.
+// float -> bf16 bits, round to nearest even (gfx950's v_cvt_pk_bf16_f32; a NaN stays a
+// quiet NaN).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
 // ---------------------------------------------------------------------------- e4m3
@@ -52,7 +52,7 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
 
 // ---------------------------------------------------------------------------- math
 
-__device__ __forceinline__ float silu_fast(float z) { return z / (1.0f + __expf(-z)); }
+__device__ __forceinline__ float silu_fast(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 __device__ __forceinline__ float silu_exact(float z) { return z / (1.0f + expf(-z)); }
 // GELU in its exact form z * Phi(z) = z / 2 * erfc(-z / sqrt 2) (erfc keeps the far negative
 // tail accurate), and ReLU: the gates of GeGLU and ReGLU
@@ -60,7 +60,10 @@ __device__ __forceinline__ float gelu_exact(float z) { return 0.5f * z * erfcf(-
 __device__ __forceinline__ float relu_gate(float z) { return z > 0.0f ? z : 0.0f; }
 
 // The gate function of the gated activation a = gate(g) * u: SwiGLU (silu, the default),
-// GeGLU (gelu) or ReGLU (relu).  FAST: silu on the hardware exp (for bf16 results).
+// GeGLU (gelu) or ReGLU (relu).  FAST: silu on the hardware exp and reciprocal (a few float32
+// ulps from the exact quotient, where the libm exp and an IEEE division cost about three times
+// the instructions): for bf16 results and for the e4m3 requantization of the SwiGLU rows,
+// whose float32 input already carries the block-scaled MFMA's accumulation error.
 enum { kGateSilu = 0, kGateGelu = 1, kGateRelu = 2 };
 template <bool FAST>
 __device__ __forceinline__ float gate_fn(int gate, float z) {
