@@ -268,14 +268,16 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_fp8_kernel(GroupedArgs g)
       issue(0, 0);
       if (1 < KT) issue(1, 1);
       int slot = 0;
-      for (int kt = 0; kt < KT; ++kt) {
-        if (kt + 1 < KT) wait_one_slice();
-        else wait_vmcnt<0>();
+      for (int kt = 0; kt + 1 < KT; ++kt) {
+        wait_one_slice();
         __syncthreads();
         const int nslot = slot == 0 ? 2 : slot - 1;
         compute(NI_, kt, slot, kt + 2 < KT, nslot);
         slot = slot == 2 ? 0 : slot + 1;
       }
+      wait_vmcnt<0>();   // the last slice
+      __syncthreads();
+      compute(NI_, KT - 1, slot, false, 0);
     };
     __syncthreads();   // sSb of this item is visible
     switch ((nfr16 - wm + 1) / 2) {
@@ -314,13 +316,18 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_fp8_kernel(GroupedArgs g)
         }
       }
       __syncthreads();
+      // every lane stores in every round (lanes past the end repeat the last piece inside
+      // the matrix), so the loop has no divergent branch
       uint16_t* out = reinterpret_cast<uint16_t*>(g.slot_out);
-      for (int c = tid; c < rows * (BN / 8); c += kThreads) {
-        const int r = c / (BN / 8), piece = c % (BN / 8);
+      const int npieces = rows * (BN / 8);
+      const int last_piece = min(BN / 8, (ncols - nt * BN) / 8) - 1;
+      const int nround = (npieces + kThreads - 1) / kThreads;
+      for (int q = 0; q < nround; ++q) {
+        const int c = min(q * kThreads + tid, npieces - 1);
+        const int r = c / (BN / 8), piece = min(c % (BN / 8), last_piece);
         const int col = nt * BN + piece * 8;
-        if (col < ncols)
-          *reinterpret_cast<i32x4*>(out + (int64_t)sTok[r] * g.H + col) =
-              *reinterpret_cast<const i32x4*>(stage + r * BN + piece * 8);
+        *reinterpret_cast<i32x4*>(out + (int64_t)sTok[r] * g.H + col) =
+            *reinterpret_cast<const i32x4*>(stage + r * BN + piece * 8);
       }
     } else {
       if (tid < BM) {
