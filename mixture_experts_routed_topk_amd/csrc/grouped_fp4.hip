@@ -225,23 +225,27 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_fp4_kernel(GroupedArgs g)
         bf[j] = *reinterpret_cast<const i32x4*>(Bs + c * BROW + (b_chunk(c, g4) << 4));
         sbv[j] = Sb[c * 4 + g4];
       }
+      // four independent block products per row fragment (the MFMAs write distinct
+      // registers and issue back to back); those of fragment i are folded after the MFMAs
+      // of fragment i + 1 are issued, so the folds never wait for the products they read
+      f32x4 pr[2][NFRAG], sc[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 5; ++i) {
         if (i < NI) {
           const char* ap = As + (2 * i + wm) * 16 * AROW;
           const i32x4 lo = *reinterpret_cast<const i32x4*>(ap + foff0);
           const i32x4 hi = *reinterpret_cast<const i32x4*>(ap + foff1);
           const i32x8 af = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          const f32x4 sa = *reinterpret_cast<const f32x4*>(&Sa[(2 * i + wm) * 16 + 4 * g4]);
-          // four independent block products first, then their folds (the MFMAs write
-          // distinct registers and issue back to back)
-          f32x4 pr[NFRAG];
+          sc[i & 1] = *reinterpret_cast<const f32x4*>(&Sa[(2 * i + wm) * 16 + 4 * g4]);
 #pragma unroll
-          for (int j = 0; j < NFRAG; ++j) pr[j] = mfma_16x16x128_e4m3_e2m1(af, bf[j], sbv[j]);
+          for (int j = 0; j < NFRAG; ++j) pr[i & 1][j] = mfma_16x16x128_e4m3_e2m1(af, bf[j], sbv[j]);
+        }
+        if (i >= 1 && i - 1 < NI) {
+          const int ip = i - 1;
 #pragma unroll
           for (int j = 0; j < NFRAG; ++j)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc[i][j][q] = fmaf(pr[j][q], sa[q], acc[i][j][q]);
+            for (int q = 0; q < 4; ++q) acc[ip][j][q] = fmaf(pr[ip & 1][j][q], sc[ip & 1][q], acc[ip][j][q]);
         }
         if (next && i < 3) issue_part(kt + 2, nslot, i);
       }

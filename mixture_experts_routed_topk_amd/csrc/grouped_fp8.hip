@@ -237,31 +237,35 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_fp8_kernel(GroupedArgs g)
         const i32x4 hi = *reinterpret_cast<const i32x4*>(bp + foff1);
         bf[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
+      // four independent block products per row fragment (each MFMA writes its own
+      // registers, so they issue back to back); those of fragment i are folded after the
+      // MFMAs of fragment i + 1 are issued, so the folds never wait for the products they read
+      f32x4 pr[2][NFRAG], sc[2][2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 5; ++i) {
         if (i < NI) {
           const char* ap = As + (2 * i + wm) * 16 * ROWB;
           const i32x4 lo = *reinterpret_cast<const i32x4*>(ap + foff0);
           const i32x4 hi = *reinterpret_cast<const i32x4*>(ap + foff1);
           const i32x8 af = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           const f32x4 sa = *reinterpret_cast<const f32x4*>(&Sa[(2 * i + wm) * 16 + 4 * g4]);
-          f32x4 s0, s1;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            s0[q] = sa[q] * sb0;
-            s1[q] = sa[q] * sb1;
+            sc[i & 1][0][q] = sa[q] * sb0;
+            sc[i & 1][1][q] = sa[q] * sb1;
           }
-          // four independent block products first, then their folds: each MFMA writes its
-          // own registers, so the next one issues without waiting for the previous fold
-          f32x4 pr[NFRAG];
 #pragma unroll
-          for (int j = 0; j < NFRAG; ++j) pr[j] = mfma_16x16x128_e4m3(af, bf[j], f32x4{});
+          for (int j = 0; j < NFRAG; ++j) pr[i & 1][j] = mfma_16x16x128_e4m3(af, bf[j], f32x4{});
+        }
+        if (i >= 1 && i - 1 < NI) {
+          const int ip = i - 1;
 #pragma unroll
           for (int j = 0; j < NFRAG; ++j)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc[i][j][q] = fmaf(pr[j][q], j < 2 ? s0[q] : s1[q], acc[i][j][q]);
+            for (int q = 0; q < 4; ++q)
+              acc[ip][j][q] = fmaf(pr[ip & 1][j][q], sc[ip & 1][j < 2 ? 0 : 1][q], acc[ip][j][q]);
         }
-        if (next) issue_part(kt + 2, nslot, i);
+        if (i < 4 && next) issue_part(kt + 2, nslot, i);
       }
     };
     auto kloop = [&](auto NI_) __attribute__((always_inline)) {
