@@ -70,9 +70,9 @@ enum {
   /* Bit-reproducible combine at every size: each slot's weighted expert output is
    * written to its own row and the k rows of a token are summed in slot order.
    * Without the flag this combine is used while the slot rows are small (float32
-   * rows, 4*T*k*H bytes, at most 512 MiB; the bf16 rows of a bf16 layer, 2*T*k*H
-   * bytes, at most 1 GiB), and floating-point atomic adds into a [T, H] accumulator
-   * above (or always with MOE_FLAG_ATOMIC_COMBINE). */
+   * rows, 4*T*k*H bytes, at most 512 MiB; the bf16 rows of a bf16, fp8 or fp4 layer
+   * on the grouped path, 2*T*k*H bytes, at most 1 GiB), and floating-point atomic adds
+   * into a [T, H] accumulator above (or always with MOE_FLAG_ATOMIC_COMBINE). */
   MOE_FLAG_DETERMINISTIC = 2u,
   /* Path selection (both give the same result within tolerance): the grouped
    * path sorts slots by expert and runs grouped GEMMs; the decode path streams
