@@ -60,13 +60,21 @@ __global__ __launch_bounds__(kThreads) void finalize_slots_kernel(const R* __res
     const int64_t t = i / h8;
     const int c = (int)(i - t * h8) * 8;
     float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const int64_t slot = t * k + j;
-      if (inv[slot] < 0) continue;
-      float v[8];
-      load8(rows, slot * H + c, v);
+    // four slots at a time: their rows are loaded together (a dropped slot's row too, and
+    // then not added), and added in slot order
+    for (int j0 = 0; j0 < k; j0 += 4) {
+      bool use[4];
+      float v[4][8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) s[q] += v[q];
+      for (int jj = 0; jj < 4; ++jj) use[jj] = j0 + jj < k && inv[t * k + j0 + jj] >= 0;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) load8(rows, (t * k + min(j0 + jj, k - 1)) * H + c, v[jj]);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        if (use[jj]) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) s[q] += v[jj][q];
+        }
     }
     if (out_bf16) {
       uint4 o;
