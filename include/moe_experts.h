@@ -287,8 +287,13 @@ moe_status moe_plan_describe(const moe_problem* p, char* buf, size_t len);
  *   fmt 1: a as above, b [nblocks][16][64] bytes of e2m1 codes (element k in the low
  *          nibble of byte k/2 for even k), b_scale [nblocks][16][4] UE8M0 exponents (one
  *          per column and 32-long k block);
+ *   fmt 2: a and b as for fmt 0, b_scale [nblocks][16][4] UE8M0 bytes passed as the
+ *          instruction's B scales by lane (column, k block) as for fmt 1; only one
+ *          exponent per block (all 64 equal, as the e4m3 kernels pass UE8M0 weight
+ *          scales) has a defined result;
  *   d [nblocks][16][16] float32 out: d[i][r][n] = sum_k a[i][r][k] * b[i][n][k] (fmt 1:
- *          times 2^(b_scale[i][n][k/32] - 127)).
+ *          times 2^(b_scale[i][n][k/32] - 127); fmt 2: times 2^(s - 127), s the block's
+ *          exponent).
  * Device pointers; a and b 16-byte aligned.  Errors: UNSUPPORTED (fmt), BAD_SHAPE,
  * NULL_ARG, HIP.  Asynchronous on `stream`.
  */

@@ -349,17 +349,19 @@ def quantize_rows_fp8(x: torch.Tensor):
 
 def check_mfma_blocks(a: torch.Tensor, b: torch.Tensor, b_scale: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Block products on the kernels' block-scaled MFMA (moe_check_mfma_blocks): a uint8
-    [n,16,128] e4m3 codes; b uint8 [n,16,128] e4m3 codes, or [n,16,64] packed e2m1 with
-    b_scale uint8 [n,16,4] UE8M0.  Returns float32 [n,16,16]."""
-    fmt = 0 if b_scale is None else 1
+    [n,16,128] e4m3 codes; b uint8 [n,16,128] e4m3 codes (with an optional b_scale), or
+    [n,16,64] packed e2m1 with b_scale; b_scale uint8 [n,16,4] UE8M0.  Returns float32
+    [n,16,16]."""
+    fmt = 0 if b_scale is None else (2 if b.dim() == 3 and b.shape[-1] == 128 else 1)
     for name, t in (("a", a), ("b", b)) + ((("b_scale", b_scale),) if fmt else ()):
         _need_gpu(name, t)
         if t.dtype != torch.uint8:
             raise ValueError(f"{name} must be uint8")
     n = a.shape[0]
-    want_b = (n, 16, 128) if fmt == 0 else (n, 16, 64)
+    want_b = (n, 16, 64) if fmt == 1 else (n, 16, 128)
     if tuple(a.shape) != (n, 16, 128) or tuple(b.shape) != want_b or (fmt and tuple(b_scale.shape) != (n, 16, 4)):
-        raise ValueError("shapes: a [n,16,128], b [n,16,128] (e4m3) or [n,16,64] with b_scale [n,16,4] (e2m1)")
+        raise ValueError("shapes: a [n,16,128], b [n,16,128] (e4m3, b_scale optional) or [n,16,64] with "
+                         "b_scale [n,16,4] (e2m1)")
     d = torch.empty((n, 16, 16), dtype=torch.float32, device=a.device)
     _check(lib().moe_check_mfma_blocks(fmt, _ptr(a), _ptr(b), _ptr(b_scale), _ptr(d), n, _stream(a.device)))
     return d

@@ -645,10 +645,10 @@ moe_status moe_quantize_rows_fp8(const void* x_bf16, int64_t rows, int32_t cols,
 
 moe_status moe_check_mfma_blocks(int fmt, const uint8_t* a, const uint8_t* b, const uint8_t* b_scale, float* d,
                                  int nblocks, void* stream) {
-  if (fmt != 0 && fmt != 1) return MOE_ERR_UNSUPPORTED;
+  if (fmt < 0 || fmt > 2) return MOE_ERR_UNSUPPORTED;
   if (nblocks < 0) return MOE_ERR_BAD_SHAPE;
   if (nblocks == 0) return MOE_OK;
-  if (!a || !b || !d || (fmt == 1 && !b_scale)) return MOE_ERR_NULL_ARG;
+  if (!a || !b || !d || (fmt != 0 && !b_scale)) return MOE_ERR_NULL_ARG;
   if (!aligned16(a) || !aligned16(b) || !aligned4(d)) return MOE_ERR_BAD_SHAPE;
   (void)hipGetLastError();  // see moe_experts_forward
   MOE_HIP_CHECK(launch_mfma_block_check(a, b, b_scale, d, nblocks, fmt, static_cast<hipStream_t>(stream)));

@@ -8,7 +8,9 @@
 // row m and weight row n
 //     y[m, n] = sum over 128-blocks kb of  sa[m, kb] * sw[n, kb] * sum_{k in kb} a[m, k] w[n, k]
 // The inner sum of one block is one 16x16x128 e4m3 MFMA; its result is folded into the
-// float32 accumulator times the two scales.
+// float32 accumulator times the two scales.  With UE8M0 weight scales the MFMA applies sw
+// itself (its block-scale operand: a power of two, exact), so the fold multiplies by sa
+// alone -- the same value, one multiplication fewer per row and block.
 //
 // gate_up: a tile's 256 weight rows are 128 gate rows and the matching 128 up rows, so the
 // epilogue forms gate(g) * u for 128 SwiGLU columns in registers -- one activation scale
@@ -62,13 +64,17 @@ enum { kGateUp = 0, kDownAtomic = 1, kDownSlots = 2, kDownSlotsBf16 = 3 };
 
 __device__ __forceinline__ int chunk_slot(int row, int c) { return c ^ ((row >> 1) & 7); }
 
-__device__ __forceinline__ float ue8m0_value(uint32_t b) {
-  if (b == 0) return __uint_as_float(0x00400000u);   // 2^-127
-  if (b == 255) return __uint_as_float(0x7fc00000u);
-  return __uint_as_float(b << 23);
+// mfma_16x16x128_e4m3 with the whole B block scaled by 2^(s - 127): every lane passes the
+// same UE8M0 byte s as the instruction's B scale.  (The instruction takes one scale per
+// column and 32-long k block from the lanes; which lane feeds which differs between operand
+// formats, and with one exponent for the block it does not matter.)  A power-of-two scale is
+// exact, so the result is the unit-scale one times it.
+__device__ __forceinline__ f32x4 mfma_16x16x128_e4m3_sb(i32x8 a, i32x8 b, int scale_b) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, f32x4{}, 0, 0, 0, 127, 0, scale_b);
 }
 
-template <int MODE>
+
+template <int MODE, bool UE8>
 __global__ __launch_bounds__(kThreads, 1) void grouped_fp8_kernel(GroupedArgs g) {
   __shared__ __attribute__((aligned(1024))) char ring[NSTAGE][STAGE];
   __shared__ float sSb[2][kMaxKB];          // the item's weight block scales (two row blocks)
@@ -159,8 +165,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_fp8_kernel(GroupedArgs g)
         const int hb = i < KB ? 0 : 1;
         const int kb = i - hb * KB;
         const int64_t blk = (int64_t)e * nblk_rows + b_row(128 * hb) / 128;
-        float v;
-        if (g.b_scale_ue8m0) v = ue8m0_value(static_cast<const uint8_t*>(g.b_scale)[blk * KB + kb]);
+        float v;   // UE8: the exponent byte itself (bits of the float), for the MFMA
+        if (UE8) v = __int_as_float((int)static_cast<const uint8_t*>(g.b_scale)[blk * KB + kb]);
         else v = static_cast<const float*>(g.b_scale)[blk * KB + kb];
         sSb[hb][kb] = v;
       }
@@ -229,6 +235,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_fp8_kernel(GroupedArgs g)
       // block; gate_up, fragments 0, 1 are gate rows and 2, 3 the matching up rows
       const float sb0 = sSb[MODE == kGateUp ? 0 : wn >> 1][kt];
       const float sb1 = sSb[MODE == kGateUp ? 1 : wn >> 1][kt];
+      const int eb0 = __float_as_int(sb0), eb1 = __float_as_int(sb1);   // (UE8)
       i32x8 bf[NFRAG];
 #pragma unroll
       for (int j = 0; j < NFRAG; ++j) {
@@ -251,11 +258,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_fp8_kernel(GroupedArgs g)
           const f32x4 sa = *reinterpret_cast<const f32x4*>(&Sa[(2 * i + wm) * 16 + 4 * g4]);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            sc[i & 1][0][q] = sa[q] * sb0;
-            sc[i & 1][1][q] = sa[q] * sb1;
+            sc[i & 1][0][q] = UE8 ? sa[q] : sa[q] * sb0;
+            sc[i & 1][1][q] = UE8 ? sa[q] : sa[q] * sb1;
           }
 #pragma unroll
-          for (int j = 0; j < NFRAG; ++j) pr[i & 1][j] = mfma_16x16x128_e4m3(af, bf[j], f32x4{});
+          for (int j = 0; j < NFRAG; ++j)
+            pr[i & 1][j] = UE8 ? mfma_16x16x128_e4m3_sb(af, bf[j], j < 2 ? eb0 : eb1)
+                               : mfma_16x16x128_e4m3(af, bf[j], f32x4{});
         }
         if (i >= 1 && i - 1 < NI) {
           const int ip = i - 1;
@@ -366,7 +375,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_fp8_kernel(GroupedArgs g)
 template <int MODE>
 hipError_t launch(const GroupedArgs& g, int grid, hipStream_t s) {
   if (g.K / ROWB > kMaxKB) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((grouped_fp8_kernel<MODE>), dim3(grid), dim3(kThreads), 0, s, g);
+  if (g.b_scale_ue8m0)
+    hipLaunchKernelGGL((grouped_fp8_kernel<MODE, true>), dim3(grid), dim3(kThreads), 0, s, g);
+  else
+    hipLaunchKernelGGL((grouped_fp8_kernel<MODE, false>), dim3(grid), dim3(kThreads), 0, s, g);
   return hipGetLastError();
 }
 

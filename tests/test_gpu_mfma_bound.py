@@ -112,3 +112,30 @@ def test_e4m3_e2m1_block_bound(spread):
     r = _worst_ratio(d, prod)
     print(f"e4m3 x e2m1 exponents {spread}: max |mfma - exact| / max|product| = 2^{np.log2(max(r, 1e-300)):.2f}")
     assert r <= MFMA_BLOCK_BOUND
+
+
+
+@pytest.mark.parametrize("spread", [(120, 135), (100, 150)])
+def test_e4m3_scaled_block_bound(spread):
+    """e4m3 x e4m3 with one UE8M0 exponent on B for the whole block, passed by every lane:
+    how the e4m3 kernels apply UE8M0 weight scales (a 128 x 128 weight block is one exponent).
+    The result is the exact sum times 2^(s - 127) within the block bound, and bit for bit the
+    unit-scale result times that power of two.  (Which lane's byte scales which column and
+    32-block differs between the operand formats; with one exponent for the block it does not
+    matter, and the kernels rely on nothing else.)"""
+    rng = np.random.default_rng(spread[1] + 7)
+    a = _rows_like_quantised(rng, (N, 16, 128))
+    b = _rows_like_quantised(rng, (N, 16, 128)) if spread[1] < 140 else _finite_codes(rng, (N, 16, 128))
+    s_blk = rng.integers(spread[0], spread[1], N).astype(np.uint8)
+    sb = np.ascontiguousarray(np.broadcast_to(s_blk[:, None, None], (N, 16, 4)))
+    ta, tb = torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda()
+    d = m.check_mfma_blocks(ta, tb, torch.from_numpy(sb).cuda()).cpu().numpy()
+    d0 = m.check_mfma_blocks(ta, tb).cpu().numpy()
+    scale = ue8m0_decode(s_blk).astype(np.float64)[:, None, None]
+    av = e4m3_decode(a).reshape(a.shape)
+    bv = e4m3_decode(b).reshape(b.shape)
+    prod = av[:, :, None, :] * bv[:, None, :, :] * scale[..., None]   # exact in fp64
+    r = _worst_ratio(d, prod)
+    print(f"e4m3 x e4m3, block exponents {spread}: max |mfma - exact| / max|product| = 2^{np.log2(max(r, 1e-300)):.2f}")
+    assert r <= MFMA_BLOCK_BOUND
+    assert np.array_equal(d.astype(np.float64), d0.astype(np.float64) * scale)
