@@ -294,3 +294,15 @@ def test_noalloc_rejects_problems_beyond_its_array_before_any_hip_call():
                                          None) == m.ERR_NULL_ARG
     t0 = P(act=m.BF16, weight=m.BF16, T=0)
     assert L.moe_experts_forward_noalloc(ctypes.byref(t0), None, None, None, None, None, None, None, None, None) == m.OK
+
+
+def test_check_mfma_blocks_rejects_before_any_hip_call():
+    L = m.lib()
+    a, b, s, d = ctypes.c_void_p(4096), ctypes.c_void_p(8192), ctypes.c_void_p(12288), ctypes.c_void_p(16384)
+    assert L.moe_check_mfma_blocks(3, a, b, s, d, 4, None) == m.ERR_UNSUPPORTED
+    assert L.moe_check_mfma_blocks(-1, a, b, s, d, 4, None) == m.ERR_UNSUPPORTED
+    assert L.moe_check_mfma_blocks(0, a, b, None, d, -1, None) == m.ERR_BAD_SHAPE
+    assert L.moe_check_mfma_blocks(2, a, b, None, d, 4, None) == m.ERR_NULL_ARG    # fmt 2 needs exponents
+    assert L.moe_check_mfma_blocks(1, a, b, None, d, 4, None) == m.ERR_NULL_ARG
+    assert L.moe_check_mfma_blocks(2, ctypes.c_void_p(4100), b, s, d, 4, None) == m.ERR_BAD_SHAPE   # a not 16-byte aligned
+    assert L.moe_check_mfma_blocks(2, a, b, s, d, 0, None) == m.OK                # nothing to do, no launch
