@@ -67,3 +67,13 @@ def test_qwen_prefill_algorithmic_counts():
     lf, lb = bench.layer_totals(spec, 60)
     assert lf == 6.0 * 16384 * 2048 * 1408
     assert lb == 60 * 3 * 1408 * 2048 * 2 + 2 * 4096 * 2048 * 2 + 8 * 16384
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(bench.ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120, cwd=bench.ROOT)
+    assert r.returncode != 0
+    assert "one GPU only" in r.stderr
+    assert r.stdout.strip() == ""          # no JSON line
