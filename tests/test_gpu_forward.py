@@ -55,8 +55,10 @@ def _record(entry: dict):
             fh.write(json.dumps(entry) + "\n")
 
 
-def _full_check(spec, flags, tokens=None, what="", threads=16):
-    D = device_layer(spec)
+def _full_check(spec, flags, tokens=None, what="", threads=16, D=None):
+    """GPU forward of `spec` (staged by device_layer, or the given layer D with its keys) against
+    the oracle on `tokens` (all by default), fp8 / fp4 requantised rows checked first."""
+    D = device_layer(spec) if D is None else D
     quant = spec.weight in ("fp8", "fp4")
     prob = m.problem_for(D["x"], D["idx"], D["w_gate_up"], D["w_down"], D.get("w_gate_up_scale"), flags)
     ws = torch.empty(m.workspace_size(prob), dtype=torch.uint8, device=D["x"].device)
