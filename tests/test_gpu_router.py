@@ -48,3 +48,26 @@ def test_route_logits_empty_and_bad_k():
     assert idx.shape == (0, 2) and (c.cpu() == 0).all() and (o.cpu() == 0).all()
     with pytest.raises(ValueError):
         m.route_logits(torch.zeros((4, 100), dtype=torch.float32, device="cuda"), 65)
+
+
+@pytest.mark.parametrize("E,k,renorm", [(16, 4, False), (256, 8, True)])
+def test_router_then_forward(E, k, renorm):
+    """Logits -> the library's router -> the experts forward on its ids and weights, against
+    the oracle's router and forward from the same logits (the whole layer after the gate)."""
+    import synth
+    from synth.device import host_to_tensor
+    from moe_helpers import assert_close, gpu_out_f64, oracle_out, oracle_weights
+    spec = synth.Spec(f"router_forward_{E}", T=300, H=256, I=256, E=E, k=k, act="bf16", weight="bf16", seed=E + k)
+    lg = _logits(spec.T, E, seed=E * 3 + k, ties=True, masked=True)
+    idx, w, *_ = m.route_logits(torch.from_numpy(lg).cuda(), k, renorm)
+    x = synth.hidden(spec)
+    X = host_to_tensor(x, "bf16").cuda()
+    ridx, rw = router_topk(lg, k, renorm)
+    active = np.unique(ridx)
+    gu = np.zeros((E, 2 * spec.I, spec.H), np.uint16)
+    dn = np.zeros((E, spec.H, spec.I), np.uint16)
+    for e in active:
+        gu[e], dn[e] = synth.expert_gate_up(spec, e), synth.expert_down(spec, e)
+    out = m.experts_forward(X, idx, w, host_to_tensor(gu, "bf16").cuda(), host_to_tensor(dn, "bf16").cuda())
+    ref = oracle_out(spec, x, ridx, rw.astype(np.float32), oracle_weights(spec))
+    assert_close(gpu_out_f64(out), ref, "bf16", f"router + forward, E={E}, k={k}")
