@@ -79,3 +79,50 @@ def test_forward_replays_in_a_graph(case):
     torch.cuda.synchronize()
     ref2 = oracle_out(spec, D["x_host"], idx2, w2, weights)
     assert_close(gpu_out_f64(out), ref2, "bf16", f"{case}: replay with a new routing")
+
+
+@pytest.mark.parametrize("weight,scale,flags", [
+    ("fp8", "f32", m.FLAG_DETERMINISTIC), ("fp8", "ue8m0", 0), ("fp4", "ue8m0", m.FLAG_DETERMINISTIC),
+    ("fp4", "ue8m0", m.FLAG_ATOMIC_COMBINE),
+])
+def test_quantised_forward_replays_in_a_graph(weight, scale, flags):
+    """The e4m3 and FP4 forwards (x quantization, gate_up with the requantising epilogue, down,
+    combine) captured once and replayed with eager work in between: every replay equals the
+    eager call (bit for bit with the per-slot combine, within float-atomic reordering, far
+    inside the tolerance, with the atomic one).  The eager call's parity with the oracle is
+    test_gpu_forward's."""
+    spec = synth.Spec(f"graph_{weight}", T=160, H=256, I=256, E=6, k=2, act="bf16", weight=weight, scale=scale,
+                      seed=23)
+    D = device_layer(spec, poison_inactive=False)
+    prob = m.problem_for(D["x"], D["idx"], D["w_gate_up"], D["w_down"], D["w_gate_up_scale"], flags)
+    ws = torch.empty(m.workspace_size(prob), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(D["x"])
+
+    def fwd():
+        m.experts_forward(D["x"], D["idx"], D["w"], D["w_gate_up"], D["w_down"], D["w_gate_up_scale"],
+                          D["w_down_scale"], out=out, flags=flags, workspace=ws)
+
+    fwd()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fwd()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fwd()
+    torch.cuda.synchronize()
+    for i in range(3):
+        out.fill_(0.0)
+        ws.fill_(0xA5)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        if flags & m.FLAG_ATOMIC_COMBINE:
+            d = (out.float() - eager.float()).abs()
+            assert (d <= 1e-2 * (1 + eager.float().abs())).all(), f"replay {i}: max difference {d.max().item()}"
+        else:
+            assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {i} differs"
