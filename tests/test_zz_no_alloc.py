@@ -40,6 +40,7 @@ CASES = {
     "bf16_deterministic": (dict(H=1024, I=512, E=16, k=2, act="bf16", weight="bf16"), m.FLAG_DETERMINISTIC, True),
     "bf16_decode": (dict(H=2048, I=1408, E=60, k=4, act="bf16", weight="bf16"), m.FLAG_FORCE_DECODE, True),
     "fp8_f32_scales": (dict(H=1024, I=512, E=16, k=4, act="bf16", weight="fp8", scale="f32"), 0, True),
+    "fp8_ue8m0_scales": (dict(H=1024, I=512, E=16, k=4, act="bf16", weight="fp8", scale="ue8m0"), 0, True),
     "fp4": (dict(H=1024, I=512, E=16, k=4, act="bf16", weight="fp4", scale="ue8m0"), 0, True),
     "f32": (dict(H=256, I=128, E=8, k=2, act="f32", weight="f32"), m.FLAG_FORCE_GROUPED, True),
 }
